@@ -1,0 +1,218 @@
+"""Seeded synthetic workloads for the Kimi K3 LatentMoE layer.
+
+Test and benchmark infrastructure, shared by the CPU oracle and the GPU path:
+it draws the token batch and the weights (and the skewed router bias of the
+load-imbalance workload) and holds none of the layer's arithmetic.
+
+Shapes follow the Kimi K3 course, lesson 6 "LatentMoE": model width d = 7168,
+latent width l = 3584, routed expert GLU hidden 3072, 896 routed experts with
+top-16 selection and two full-width shared experts (sections "Deriving the
+headline number" and "show me the actual equation"). Weights are drawn
+~N(0, 1/fan_in) in fp32 and stored as MXFP4 (E2M1 codes, one E8M0 scale per
+32 values along the reduction axis); x ~ N(0, 1) rounded to bf16.
+
+Tensor layout handed to both sides ("canonical MX"):
+  codes  uint8 [N, K/2]   element 2i in the low nibble
+  scales uint8 [N, K/32]  E8M0 byte
+for a matrix W[N, K] that maps K inputs to N outputs (y = W x).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass, field, replace
+from functools import lru_cache
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "k3gen.c")
+_LIB = os.path.join(_HERE, "libk3gen.so")
+
+# tensor ids of the counter-based streams
+X, W_ROUTER, W_DOWN, W_UP, GATE, UP, DOWN, SH_GATE, SH_UP, SH_DOWN, ZIPF_PERM = range(1, 12)
+
+
+def build(force: bool = True) -> str:
+    """Compile the generator with gcc (OpenMP). Returns the library path."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC",
+               "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+@lru_cache(maxsize=1)
+def _lib():
+    if not os.path.exists(_LIB):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB)
+    u64, u32, i64, i32, f32, vp = (ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int32,
+                                   ctypes.c_float, ctypes.c_void_p)
+    lib.k3gen_key.argtypes = [u64, u32, u32]
+    lib.k3gen_key.restype = u64
+    lib.k3gen_u64.argtypes = [u64, u32, u32, i64, vp]
+    lib.k3gen_normal.argtypes = [u64, u32, u32, i64, f32, vp]
+    lib.k3gen_bf16.argtypes = [u64, u32, u32, i64, f32, vp]
+    lib.k3gen_mxfp4_many.argtypes = [u64, u32, u32, i32, i64, i64, f32, vp, vp]
+    for f in (lib.k3gen_u64, lib.k3gen_normal, lib.k3gen_bf16, lib.k3gen_mxfp4_many):
+        f.restype = None
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def u64(seed: int, tensor: int, sub: int, n: int) -> np.ndarray:
+    out = np.empty(n, np.uint64)
+    _lib().k3gen_u64(seed, tensor, sub, n, _ptr(out))
+    return out
+
+
+def normal(seed: int, tensor: int, sub: int, shape, std: float = 1.0) -> np.ndarray:
+    n = int(np.prod(shape))
+    assert n % 2 == 0
+    out = np.empty(n, np.float32)
+    _lib().k3gen_normal(seed, tensor, sub, n, std, _ptr(out))
+    return out.reshape(shape)
+
+
+def bf16_normal(seed: int, tensor: int, sub: int, shape, std: float = 1.0) -> np.ndarray:
+    """Normals rounded to bf16, returned as raw uint16 bit patterns."""
+    n = int(np.prod(shape))
+    assert n % 2 == 0
+    out = np.empty(n, np.uint16)
+    _lib().k3gen_bf16(seed, tensor, sub, n, std, _ptr(out))
+    return out.reshape(shape)
+
+
+def mxfp4(seed: int, tensor: int, sub0: int, N: int, K: int, std: float, count: int | None = None):
+    """MXFP4 matrices [N, K] ~ N(0, std^2); with `count`, a stack of `count` of them
+    from subs sub0..sub0+count-1. Returns (codes, scales)."""
+    assert K % 32 == 0
+    c = 1 if count is None else count
+    codes = np.empty((c, N, K // 2), np.uint8)
+    scales = np.empty((c, N, K // 32), np.uint8)
+    _lib().k3gen_mxfp4_many(seed, tensor, sub0, c, N, K, std, _ptr(codes), _ptr(scales))
+    if count is None:
+        return codes[0], scales[0]
+    return codes, scales
+
+
+# --------------------------------------------------------------------------------------------
+# Workload registry
+# --------------------------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class LayerShape:
+    d: int          # model width
+    l: int          # latent width (== d when latent_moe is 0)
+    h: int          # routed expert GLU hidden
+    E: int          # routed experts
+    k: int          # experts selected per token
+    Ns: int         # shared experts
+    hs: int         # shared expert GLU hidden
+    latent_moe: int = 1   # 1: eq. 11 LatentMoE; 0: conventional full-width MoE
+    act: str = "bf16"     # activation format of the routed GEMM inputs: "bf16" | "mxfp8"
+    eps: float = 1e-6
+
+    @property
+    def expert_in(self) -> int:
+        """Width the routed experts work in."""
+        return self.l if self.latent_moe else self.d
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    shape: LayerShape
+    T: int
+    seed: int
+    bias: str = "zero"        # "zero" | "zipf"
+    zipf_alpha: float = 1.5   # b_e = alpha * ln(w_e), w_e Zipf(s=1) weight of expert e's rank
+    note: str = ""
+
+    # ---- inputs -----------------------------------------------------------------------------
+    def x_bits(self, T: int | None = None) -> np.ndarray:
+        """x [T, d] bf16 bits; rows are the first T rows of the full batch."""
+        T = self.T if T is None else T
+        return bf16_normal(self.seed, X, 0, (T, self.shape.d))
+
+    def router_bias(self) -> np.ndarray:
+        s = self.shape
+        if self.bias == "zero":
+            return np.zeros(s.E, np.float32)
+        # random expert order from the stream; expert at rank r gets Zipf weight 1/(r+1)
+        order = np.argsort(u64(self.seed, ZIPF_PERM, 0, s.E), kind="stable")
+        rank = np.empty(s.E, np.int64)
+        rank[order] = np.arange(s.E)
+        w = 1.0 / (rank + 1.0)
+        return (self.zipf_alpha * np.log(w)).astype(np.float32)
+
+    def rms_gamma(self) -> np.ndarray:
+        return np.ones(self.shape.l, np.float32)
+
+    # ---- weights (canonical MX); std = 1/sqrt(fan_in) -----------------------------------------
+    def w_router(self):
+        s = self.shape
+        return mxfp4(self.seed, W_ROUTER, 0, s.E, s.d, s.d ** -0.5)
+
+    def w_down(self):
+        s = self.shape
+        return mxfp4(self.seed, W_DOWN, 0, s.l, s.d, s.d ** -0.5)
+
+    def w_up(self):
+        s = self.shape
+        return mxfp4(self.seed, W_UP, 0, s.d, s.l, s.l ** -0.5)
+
+    def routed(self, e0: int, count: int = 1):
+        """Experts e0..e0+count-1: (gate, up, down), each (codes[count,...], scales[count,...]).
+        gate/up [h, l'], down [l', h] with l' the expert width."""
+        s = self.shape
+        li = s.expert_in
+        g = mxfp4(self.seed, GATE, e0, s.h, li, li ** -0.5, count=count)
+        u = mxfp4(self.seed, UP, e0, s.h, li, li ** -0.5, count=count)
+        dn = mxfp4(self.seed, DOWN, e0, li, s.h, s.h ** -0.5, count=count)
+        return g, u, dn
+
+    def shared(self, j: int):
+        s = self.shape
+        g = mxfp4(self.seed, SH_GATE, j, s.hs, s.d, s.d ** -0.5)
+        u = mxfp4(self.seed, SH_UP, j, s.hs, s.d, s.d ** -0.5)
+        dn = mxfp4(self.seed, SH_DOWN, j, s.d, s.hs, s.hs ** -0.5)
+        return g, u, dn
+
+    def with_tokens(self, T: int) -> "Workload":
+        return replace(self, T=T)
+
+
+K3 = dict(d=7168, l=3584, h=3072, E=896, k=16, Ns=2, hs=3072)
+
+WORKLOADS = {
+    "tiny": Workload("tiny", LayerShape(d=256, l=128, h=96, E=16, k=4, Ns=1, hs=96), T=64, seed=0,
+                     note="tiny LatentMoE layer, CPU seconds"),
+    "k3_decode_t64": Workload("k3_decode_t64", LayerShape(**K3), T=64, seed=1,
+                              note="K3 shape decode, uniform routing (b = 0)"),
+    "k3_decode_t512_zipf": Workload("k3_decode_t512_zipf", LayerShape(**K3), T=512, seed=1, bias="zipf",
+                                    zipf_alpha=1.5,
+                                    note="K3 shape decode, literal Zipf bias b = 1.5 ln w"),
+    "k3_decode_t512_zipf_cal": Workload("k3_decode_t512_zipf_cal", LayerShape(**K3), T=512, seed=1,
+                                        bias="zipf", zipf_alpha=0.03,
+                                        note="K3 shape decode, Zipf bias scaled to a 2-10x hot-expert load"),
+    "k3_prefill_t8192": Workload("k3_prefill_t8192", LayerShape(**K3, act="mxfp8"), T=8192, seed=3,
+                                 note="K3 shape prefill chunk, MXFP8 latent and hidden activations"),
+    "fullwidth_t64": Workload("fullwidth_t64", LayerShape(d=7168, l=7168, h=3072, E=896, k=8, Ns=2, hs=3072,
+                                                          latent_moe=0), T=64, seed=4,
+                              note="conventional full-width MoE, top-8"),
+    "fullwidth_t2048": Workload("fullwidth_t2048", LayerShape(d=7168, l=7168, h=3072, E=896, k=8, Ns=2,
+                                                              hs=3072, latent_moe=0), T=2048, seed=4,
+                                note="conventional full-width MoE, top-8"),
+}
+
+
+def get(name: str) -> Workload:
+    return WORKLOADS[name]
