@@ -1,0 +1,112 @@
+// Internal interfaces between the C-ABI host code and the HIP kernels of the LatentMoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace k3 {
+
+// ---------------------------------------------------------------------------------------------
+// Packed weight layout ("panels").
+//
+// A weight matrix W[N, K] (N outputs, K reduction, MXFP4 with one E8M0 scale per 32 K) is cut
+// into panels of 64 output rows; each panel is a sequence of windows of 128 K. One panel-window
+// is 4352 bytes:
+//   bytes [0, 4096):    4 row-tiles x 64 lanes x 16 bytes. Lane l of row-tile rt holds the 32
+//                       E2M1 codes (one MX block, element 2i in the low nibble) of row
+//                       16 rt + (l % 16), K block 4 w + l / 16.
+//   bytes [4096, 4352): 64 lanes x 4 bytes; byte rt of lane l is the E8M0 scale of that block.
+// One lane's 16 bytes are exactly the operand of one MFMA lane (16x16 tiles, K split in four
+// 32-element blocks across the lane groups), and a wave reads a panel-window with five fully
+// coalesced loads. Rows past N and K blocks past K are zero.
+//
+// GLU panels (gate and up of one GLU packed together): panel p holds hidden units
+// [32 p, 32 p + 32): row-tile 0 = gate rows 32p..32p+15, 1 = up rows of the same units,
+// 2 = gate rows 32p+16..32p+31, 3 = up rows of those, so SiLU(gate) * up needs no data exchange.
+// ---------------------------------------------------------------------------------------------
+constexpr int kPanelRows = 64;
+constexpr int kWinK = 128;
+constexpr int kPanelWinBytes = 4352;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct PackSrc {
+  const uint8_t* codes;   // canonical [N][K/2]
+  const uint8_t* scales;  // canonical [N][K/32]
+  int32_t N, K;
+};
+
+struct PackJob {
+  uint8_t* dst;       // first panel of the panel group
+  int32_t wwin;       // windows per panel in this group
+  int32_t p_off;      // first panel written by this job
+  int32_t P;          // panels written by this job
+  int32_t glu;        // 1: GLU panels from src[0] (gate) and src[1] (up)
+  int32_t nseg;       // plain panels: K segments, src[s] covering K blocks [kb0[s], kb0[s] + K/32)
+  int32_t kb0[4];
+  PackSrc src[4];
+};
+
+// ---------------------------------------------------------------------------------------------
+// Panel GEMM: C[rows, panels] = A[rows, K] * W^T with an epilogue chosen per panel range.
+// ---------------------------------------------------------------------------------------------
+enum EpiMode : int32_t {
+  EPI_F32 = 0,          // fp32 out
+  EPI_BF16 = 1,         // bf16 out
+  EPI_SIGMOID = 2,      // fp32 sigmoid(v) out
+  EPI_SWIGLU_BF16 = 3,  // GLU panels: bf16 SiLU(gate) * up
+  EPI_SWIGLU_MXFP8 = 4, // GLU panels: MXFP8 of SiLU(gate) * up (blocks of 32 units)
+  EPI_MXFP8 = 5,        // MXFP8 out (blocks of 32 columns)
+  EPI_BF16_ADD = 6      // bf16(v + addend)
+};
+enum AFmt : int32_t { A_BF16 = 0, A_MXFP8 = 1 };
+
+struct EpiSeg {
+  int32_t p0, p1;         // panels [p0, p1) use this segment
+  int32_t mode;           // EpiMode
+  int32_t ncols;          // valid output columns (units for GLU modes) of the segment
+  int32_t col0;           // column offset in `out` (and `pre`, `addend`)
+  int32_t pad_;
+  void* out;              // row-major, leading dimension ldo (elements)
+  int64_t ldo;
+  uint8_t* out_scales;    // MXFP8 modes: E8M0 bytes, leading dimension ldos
+  int64_t ldos;
+  float* pre;             // optional fp32 copy of the values before quantisation (ld ldpre)
+  int64_t ldpre;
+  const float* addend;    // EPI_BF16_ADD (ld ldadd)
+  int64_t ldadd;
+};
+constexpr int kMaxSeg = 6;
+
+struct GemmArgs {
+  const uint8_t* W;        // packed panels of group 0
+  int64_t w_group_stride;  // bytes between groups' panel sets
+  int32_t P;               // panels per group
+  int32_t wwin;            // windows per panel
+  int32_t K;               // reduction length (multiple of 32)
+  int32_t a_fmt;           // AFmt
+  const void* A;           // bf16 or E4M3 codes, row-major, leading dimension lda (elements)
+  int64_t lda;
+  const uint8_t* A_scales; // MXFP8: E8M0 bytes, leading dimension ldas
+  int64_t ldas;
+  const int32_t* rowmap;   // optional: output row -> A row
+  const int32_t* offsets;  // grouped: rows of group g are [offsets[g], offsets[g+1])
+  int32_t M;               // dense: rows
+  int32_t nseg;
+  EpiSeg seg[kMaxSeg];
+};
+
+hipError_t launch_pack(const PackJob& job, hipStream_t s);
+// grouped (offsets != null): grid.y = n_groups; dense: grid.y = ceil(M / 16)
+hipError_t launch_panel_gemm(const GemmArgs& a, int ksplit, int grid_y, hipStream_t s);
+hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* idx, float* p,
+                       hipStream_t s);
+hipError_t launch_route(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* inv, hipStream_t s);
+// mode 0: n = bf16(gamma * u / sqrt(mean(u^2) + eps)) into n_out (ld ldn); mode 1: u only
+hipError_t launch_combine(const float* O, const int32_t* inv, const float* p, int T, int k, int width,
+                          const float* gamma, float eps, int mode, uint16_t* n_out, int64_t ldn, float* u_out,
+                          hipStream_t s);
+hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
+
+}  // namespace k3

@@ -1,0 +1,670 @@
+// HIP kernels (gfx950 / CDNA4) of the Kimi K3 LatentMoE layer forward.
+//
+// Method: Kimi K3 course, lesson 6 "LatentMoE", eq. 11 (layer) and eq. 13 (router).
+// Number formats: MXFP4 weights (E2M1 + E8M0 per 32), bf16 or MXFP8 (E4M3 + E8M0 per 32)
+// activations, fp32 accumulation.
+#include "k3moe_internal.h"
+
+#include <math.h>
+
+namespace k3 {
+
+typedef uint32_t u32;
+typedef uint16_t u16;
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+
+// ---------------------------------------------------------------------------------------------
+// scalar helpers
+// ---------------------------------------------------------------------------------------------
+
+// 2^(byte - 127) as fp32 (byte 0 -> 2^-127, a subnormal).
+__device__ __forceinline__ float e8m0_f32(u32 byte) {
+  return __uint_as_float(byte ? (byte << 23) : 0x00400000u);
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ u32 bf16_rne(float f) {
+  u32 b = __float_as_uint(f);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// E4M3 ("fn") code of x (already divided by its block scale): round to nearest even on the
+// E4M3 grid, saturate at 448, keep the sign (also of a zero result).
+__device__ __forceinline__ u32 e4m3_code(float x) {
+  u32 sign = (__float_as_uint(x) >> 24) & 0x80u;
+  float a = fabsf(x);
+  u32 code;
+  if (a < 0x1p-6f) {
+    code = (u32)rintf(a * 512.0f);  // subnormal grid step 2^-9; 8 steps = smallest normal (code 8)
+  } else {
+    u32 b = __float_as_uint(a);
+    b = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;  // keep 3 mantissa bits, ties to even
+    float r = fminf(__uint_as_float(b), 448.0f);
+    b = __float_as_uint(r);
+    code = ((((b >> 23) & 0xFFu) - 127u + 7u) << 3) | ((b >> 20) & 7u);
+  }
+  return sign | code;
+}
+
+// E8M0 byte of an MX block with largest magnitude amax > 0 for an element format whose largest
+// binade starts at 2^emax: exponent floor(log2 amax) - emax, clamped to [-127, 127].
+__device__ __forceinline__ int mx_shared_exp(float amax, int emax) {
+  int e = ilogbf(amax) - emax;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// ---------------------------------------------------------------------------------------------
+// Packer: canonical MXFP4 -> panels. One thread per (panel, window, lane).
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void pack_kernel(PackJob job) {
+  const int lane = threadIdx.x;
+  const int p = blockIdx.x;  // panel within the job
+  const int w = blockIdx.y;  // window
+  const int j = lane & 15, g = lane >> 4;
+  const int kb = 4 * w + g;
+  uint8_t* dst = job.dst + ((int64_t)(job.p_off + p) * job.wwin + w) * kPanelWinBytes;
+  u32 sc_word = 0;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    int si = -1, n = 0, kbl = -1;
+    if (job.glu) {
+      si = rt & 1;
+      n = 32 * p + (rt >> 1) * 16 + j;
+      kbl = kb;
+    } else {
+      n = 64 * p + 16 * rt + j;
+      for (int s = 0; s < job.nseg; ++s) {
+        int nkb = job.src[s].K / 32;
+        if (kb >= job.kb0[s] && kb < job.kb0[s] + nkb) {
+          si = s;
+          kbl = kb - job.kb0[s];
+        }
+      }
+    }
+    u32x4 v = {0u, 0u, 0u, 0u};
+    u32 sc = 0;
+    if (si >= 0) {
+      const PackSrc src = job.src[si];
+      if (n < src.N && kbl >= 0 && kbl < src.K / 32) {
+        v = *(const u32x4*)(src.codes + (int64_t)n * (src.K / 2) + (int64_t)kbl * 16);
+        sc = src.scales[(int64_t)n * (src.K / 32) + kbl];
+      }
+    }
+    *(u32x4*)(dst + rt * 1024 + lane * 16) = v;
+    sc_word |= sc << (8 * rt);
+  }
+  *(u32*)(dst + 4096 + lane * 4) = sc_word;
+}
+
+hipError_t launch_pack(const PackJob& job, hipStream_t s) {
+  if (job.P <= 0 || job.wwin <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_kernel, dim3(job.P, job.wwin), dim3(64), 0, s, job);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Panel GEMM.
+//
+// One wave computes one panel (64 weight rows) for a 16-row tile of A over its share of the
+// windows. Per window it loads the 4 KB of codes and 256 B of scales of the panel (5 coalesced
+// loads per lane) and the lane's 32 A values, converts the E2M1 codes to bf16 with their E8M0
+// scale (v_cvt_scalef32_pk_bf16_fp4, exact) and issues 16 MFMA 16x16x32 bf16. Loads run
+// NBUF - 1 windows ahead in a register ring, so each wave keeps several KB in flight.
+// MFMA lane roles: A lane (i = l % 16, g = l / 16) supplies row i, B lane (j, g) weight row j;
+// both take K elements [32 (4w + g) + 8 s, +8) in MFMA step s of window w; D lane (j, g) ends
+// with rows 4 g + r (r = 0..3), column j.
+// KSPLIT > 1: the four waves of a block split the windows of one panel and reduce through LDS.
+// ---------------------------------------------------------------------------------------------
+template <int AFMT>
+struct AWin;
+template <>
+struct AWin<A_BF16> {
+  u32x4 v[4];
+};
+template <>
+struct AWin<A_MXFP8> {
+  u32x4 v[2];
+  u32 sc;
+};
+
+struct WWin {
+  u32x4 c[4];
+  u32 sc;
+};
+
+struct WinBuf_bf16 {
+  WWin w;
+  AWin<A_BF16> a;
+};
+
+template <int AFMT>
+struct WinBuf {
+  WWin w;
+  AWin<AFMT> a;
+};
+
+// codes: panel base + lane * 16; scales: panel base + 4096 + lane * 4
+__device__ __forceinline__ void load_w(WWin& b, const uint8_t* pcode, const uint8_t* pscale, int w) {
+  const int64_t off = (int64_t)w * kPanelWinBytes;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) b.c[rt] = *(const u32x4*)(pcode + off + rt * 1024);
+  b.sc = *(const u32*)(pscale + off);
+}
+
+template <int AFMT>
+__device__ __forceinline__ void load_a(AWin<AFMT>& a, const GemmArgs& args, int64_t arow, bool valid, int kb);
+
+template <>
+__device__ __forceinline__ void load_a<A_BF16>(AWin<A_BF16>& a, const GemmArgs& args, int64_t arow, bool valid,
+                                               int kb) {
+  if (valid && kb * 32 < args.K) {
+    const u32x4* p = (const u32x4*)((const u16*)args.A + arow * args.lda + kb * 32);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a.v[s] = p[s];
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a.v[s] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <>
+__device__ __forceinline__ void load_a<A_MXFP8>(AWin<A_MXFP8>& a, const GemmArgs& args, int64_t arow, bool valid,
+                                                int kb) {
+  if (valid && kb * 32 < args.K) {
+    const u32x4* p = (const u32x4*)((const uint8_t*)args.A + arow * args.lda + kb * 32);
+    a.v[0] = p[0];
+    a.v[1] = p[1];
+    a.sc = args.A_scales[arow * args.ldas + kb];
+  } else {
+    a.v[0] = u32x4{0u, 0u, 0u, 0u};
+    a.v[1] = u32x4{0u, 0u, 0u, 0u};
+    a.sc = 127;
+  }
+}
+
+// bf16 operand of MFMA step s (K elements 8 s .. 8 s + 7 of the lane's block)
+template <int AFMT>
+__device__ __forceinline__ bf16x8 a_operand(const AWin<AFMT>& a, int s);
+
+template <>
+__device__ __forceinline__ bf16x8 a_operand<A_BF16>(const AWin<A_BF16>& a, int s) {
+  return __builtin_bit_cast(bf16x8, a.v[s]);
+}
+
+template <>
+__device__ __forceinline__ bf16x8 a_operand<A_MXFP8>(const AWin<A_MXFP8>& a, int s) {
+  const float sc = e8m0_f32(a.sc);
+  const u32 d0 = a.v[s >> 1][(s & 1) * 2 + 0];
+  const u32 d1 = a.v[s >> 1][(s & 1) * 2 + 1];
+  u32x4 r;
+  r[0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, false));
+  r[1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, true));
+  r[2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, sc, false));
+  r[3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, sc, true));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ bf16x8 fp4_operand(u32 d, float sc) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 0));
+  r[1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 1));
+  r[2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 2));
+  r[3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, sc, 3));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+template <int AFMT>
+__device__ __forceinline__ void compute_window(f32x4 (&acc)[4], const WWin& w, const AWin<AFMT>& a) {
+  bf16x8 av[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) av[s] = a_operand<AFMT>(a, s);
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const float sc = e8m0_f32((w.sc >> (8 * rt)) & 0xFFu);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 b = fp4_operand(w.c[rt][s], sc);
+      acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s], b, acc[rt], 0, 0, 0);
+    }
+  }
+}
+
+// MX encode a block of 32 values held as v0 (column j) and v1 (column 16 + j) by the 16 lanes of
+// one lane group; returns the E4M3 codes of v0, v1 and the E8M0 byte. All 64 lanes must call.
+__device__ __forceinline__ void mxfp8_block(float v0, float v1, u32& c0, u32& c1, u32& sbyte) {
+  float amax = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if (amax == 0.0f) {
+    sbyte = 0;
+    c0 = (__float_as_uint(v0) >> 24) & 0x80u;
+    c1 = (__float_as_uint(v1) >> 24) & 0x80u;
+    return;
+  }
+  const int e = mx_shared_exp(amax, 8);
+  sbyte = (u32)(e + 127);
+  const float inv = e8m0_f32((u32)(127 - e));  // 2^-e
+  c0 = e4m3_code(v0 * inv);
+  c1 = e4m3_code(v1 * inv);
+}
+
+__device__ __forceinline__ void epilogue(const GemmArgs& args, const f32x4 (&acc)[4], int panel, int mb, int r1,
+                                         int lane) {
+  int si = 0;
+  for (int s = 0; s < args.nseg; ++s)
+    if (panel >= args.seg[s].p0 && panel < args.seg[s].p1) si = s;
+  const EpiSeg& sg = args.seg[si];
+  const int j = lane & 15, gq = lane >> 4;
+  const int pl = panel - sg.p0;
+  const int mode = sg.mode;
+  if (mode == EPI_SWIGLU_BF16 || mode == EPI_SWIGLU_MXFP8 || mode == EPI_MXFP8) {
+    const bool glu = mode != EPI_MXFP8;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = mb + 4 * gq + r;
+      const bool ok = row < r1;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        // block q of the panel: 32 columns (GLU: 32 units over both pairs of row-tiles)
+        float v0, v1;
+        int c0i, c1i;  // column of v0, v1 within the segment
+        if (glu) {
+          v0 = silu(acc[0][r]) * acc[1][r];  // q selects the pair below
+          v1 = silu(acc[2][r]) * acc[3][r];
+          if (q == 1) break;                  // both unit halves handled in q == 0
+          c0i = 32 * pl + j;
+          c1i = 32 * pl + 16 + j;
+        } else {
+          v0 = acc[2 * q][r];
+          v1 = acc[2 * q + 1][r];
+          c0i = 64 * pl + 32 * q + j;
+          c1i = 64 * pl + 32 * q + 16 + j;
+        }
+        if (sg.pre && ok) {
+          if (c0i < sg.ncols) sg.pre[(int64_t)row * sg.ldpre + sg.col0 + c0i] = v0;
+          if (c1i < sg.ncols) sg.pre[(int64_t)row * sg.ldpre + sg.col0 + c1i] = v1;
+        }
+        if (mode == EPI_SWIGLU_BF16) {
+          if (ok) {
+            u16* o = (u16*)sg.out + (int64_t)row * sg.ldo + sg.col0;
+            if (c0i < sg.ncols) o[c0i] = (u16)bf16_rne(v0);
+            if (c1i < sg.ncols) o[c1i] = (u16)bf16_rne(v1);
+          }
+        } else {
+          u32 k0, k1, sb;
+          mxfp8_block(v0, v1, k0, k1, sb);
+          if (ok) {
+            uint8_t* o = (uint8_t*)sg.out + (int64_t)row * sg.ldo + sg.col0;
+            if (c0i < sg.ncols) o[c0i] = (uint8_t)k0;
+            if (c1i < sg.ncols) o[c1i] = (uint8_t)k1;
+            if (j == 0 && c0i < sg.ncols) sg.out_scales[(int64_t)row * sg.ldos + (sg.col0 + c0i) / 32] = (uint8_t)sb;
+          }
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int col = 64 * pl + 16 * rt + j;
+    if (col >= sg.ncols) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = mb + 4 * gq + r;
+      if (row >= r1) continue;
+      const float v = acc[rt][r];
+      const int64_t o = (int64_t)row * sg.ldo + sg.col0 + col;
+      if (mode == EPI_F32) {
+        ((float*)sg.out)[o] = v;
+      } else if (mode == EPI_SIGMOID) {
+        ((float*)sg.out)[o] = 1.0f / (1.0f + expf(-v));
+      } else if (mode == EPI_BF16) {
+        ((u16*)sg.out)[o] = (u16)bf16_rne(v);
+      } else {  // EPI_BF16_ADD
+        ((u16*)sg.out)[o] = (u16)bf16_rne(v + sg.addend[(int64_t)row * sg.ldadd + sg.col0 + col]);
+      }
+    }
+  }
+}
+
+template <int KSPLIT, int AFMT, int NBUF>
+__global__ __launch_bounds__(256) void panel_gemm_kernel(GemmArgs args) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  constexpr int PPB = 4 / KSPLIT;
+  const int panel = blockIdx.x * PPB + wave / KSPLIT;
+  const int ks = wave % KSPLIT;
+  const bool panel_ok = panel < args.P;
+
+  int grp = 0, r0, r1;
+  if (args.offsets) {
+    grp = blockIdx.y;
+    r0 = args.offsets[grp];
+    r1 = args.offsets[grp + 1];
+  } else {
+    r0 = blockIdx.y * 16;
+    r1 = min(r0 + 16, args.M);
+  }
+  if (r0 >= r1) return;  // uniform over the block
+
+  const int wbeg = (args.wwin * ks) / KSPLIT;
+  const int wend = (args.wwin * (ks + 1)) / KSPLIT;
+  const uint8_t* pbase = args.W + (int64_t)grp * args.w_group_stride +
+                         (int64_t)(panel_ok ? panel : 0) * args.wwin * kPanelWinBytes;
+  const uint8_t* pcode = pbase + lane * 16;
+  const uint8_t* pscale = pbase + 4096 + lane * 4;
+  const int g = lane >> 4;
+
+  __shared__ f32x4 red[KSPLIT > 1 ? (KSPLIT - 1) * 4 * 64 : 1];
+
+  for (int mb = r0; mb < r1; mb += 16) {
+    const int row = mb + (lane & 15);
+    const bool rv = row < r1;
+    const int64_t arow = rv ? (args.rowmap ? (int64_t)args.rowmap[row] : (int64_t)row) : 0;
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (panel_ok && wbeg < wend) {
+      WinBuf<AFMT> buf[NBUF];
+#pragma unroll
+      for (int i = 0; i < NBUF - 1; ++i) {
+        if (wbeg + i < wend) {
+          load_w(buf[i].w, pcode, pscale, wbeg + i);
+          load_a<AFMT>(buf[i].a, args, arow, rv, 4 * (wbeg + i) + g);
+        }
+      }
+      for (int w0 = wbeg; w0 < wend; w0 += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+          const int w = w0 + u;
+          if (w < wend) {
+            const int wn = w + NBUF - 1;
+            if (wn < wend) {
+              load_w(buf[(u + NBUF - 1) % NBUF].w, pcode, pscale, wn);
+              load_a<AFMT>(buf[(u + NBUF - 1) % NBUF].a, args, arow, rv, 4 * wn + g);
+            }
+            compute_window<AFMT>(acc, buf[u].w, buf[u].a);
+          }
+        }
+      }
+    }
+
+    if constexpr (KSPLIT > 1) {
+      if (ks > 0) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) red[((ks - 1) * 4 + rt) * 64 + lane] = acc[rt];
+      }
+      __syncthreads();
+      if (ks == 0) {
+#pragma unroll
+        for (int k2 = 1; k2 < KSPLIT; ++k2)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) acc[rt] += red[((k2 - 1) * 4 + rt) * 64 + lane];
+      }
+    }
+    if (panel_ok && ks == 0) epilogue(args, acc, panel, mb, r1, lane);
+    if constexpr (KSPLIT > 1) __syncthreads();
+  }
+}
+
+hipError_t launch_panel_gemm(const GemmArgs& a, int ksplit, int grid_y, hipStream_t s) {
+  if (grid_y <= 0 || a.P <= 0) return hipSuccess;
+  constexpr int NB = 3;
+  if (ksplit == 1) {
+    dim3 grid((unsigned)ceil_div(a.P, 4), (unsigned)grid_y);
+    if (a.a_fmt == A_BF16)
+      hipLaunchKernelGGL((panel_gemm_kernel<1, A_BF16, NB>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((panel_gemm_kernel<1, A_MXFP8, NB>), grid, dim3(256), 0, s, a);
+  } else if (ksplit == 4) {
+    dim3 grid((unsigned)a.P, (unsigned)grid_y);
+    if (a.a_fmt == A_BF16)
+      hipLaunchKernelGGL((panel_gemm_kernel<4, A_BF16, NB>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((panel_gemm_kernel<4, A_MXFP8, NB>), grid, dim3(256), 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Router top-k (eq. 13): per token, the k largest keys s + b in descending order (equal keys:
+// lower expert first), and p_j = s_j / sum of the selected s. One wave per token; lane l holds
+// experts l, l + 64, ...; k rounds of lane-local best then a wave argmax.
+// ---------------------------------------------------------------------------------------------
+template <int NPER>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores, const float* __restrict__ bias,
+                                                   int T, int E, int k, int32_t* __restrict__ idx,
+                                                   float* __restrict__ p) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // uniform over the wave
+  float key[NPER], sv[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      sv[i] = scores[(int64_t)t * E + e];
+      const float kk = sv[i] + bias[e];
+      key[i] = kk == kk ? kk : -INFINITY;  // a NaN key ranks last, so k valid experts are always chosen
+    } else {
+      sv[i] = 0.0f;
+      key[i] = -INFINITY;
+    }
+  }
+  u32 taken = 0;
+  int my_e = 0;
+  float my_s = 0.0f;
+  for (int jj = 0; jj < k; ++jj) {
+    float bk = -INFINITY, bs = 0.0f;
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const int e = lane + 64 * i;
+      const bool free_ = !((taken >> i) & 1u);
+      if (free_ && e < E && (key[i] > bk || (key[i] == bk && e < be))) {
+        bk = key[i];
+        be = e;
+        bs = sv[i];
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ok = __shfl_xor(bk, off);
+      const int oe = __shfl_xor(be, off);
+      const float os = __shfl_xor(bs, off);
+      if (ok > bk || (ok == bk && oe < be)) {
+        bk = ok;
+        be = oe;
+        bs = os;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == jj) {
+      my_e = be;
+      my_s = bs;
+    }
+  }
+  float sum = lane < k ? my_s : 0.0f;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  if (lane < k) {
+    idx[(int64_t)t * k + lane] = my_e;
+    p[(int64_t)t * k + lane] = my_s / sum;
+  }
+}
+
+hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* idx, float* p,
+                       hipStream_t s) {
+  dim3 grid((unsigned)ceil_div(T, 4));
+  const int nper = (int)ceil_div(E, 64);
+  if (nper <= 1)
+    hipLaunchKernelGGL((topk_kernel<1>), grid, dim3(256), 0, s, scores, bias, T, E, k, idx, p);
+  else if (nper <= 4)
+    hipLaunchKernelGGL((topk_kernel<4>), grid, dim3(256), 0, s, scores, bias, T, E, k, idx, p);
+  else if (nper <= 14)
+    hipLaunchKernelGGL((topk_kernel<14>), grid, dim3(256), 0, s, scores, bias, T, E, k, idx, p);
+  else if (nper <= 32)
+    hipLaunchKernelGGL((topk_kernel<32>), grid, dim3(256), 0, s, scores, bias, T, E, k, idx, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Dispatch tables: counts per expert, exclusive offsets, and the expert-contiguous row order
+// (expert ascending, token ascending), without atomics whose order could change the result.
+// One block of 1024 threads walks the tokens in chunks of 64: a 64-bit LDS mask per expert marks
+// the chunk's tokens that chose it (ds_or), a token's rank inside its expert is the running
+// base of the expert plus the popcount of the mask bits below it.
+// ---------------------------------------------------------------------------------------------
+constexpr int kRouteThreads = 1024;
+constexpr int kMaxExperts = 2048;
+
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+                                                              int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  __shared__ unsigned long long mask[kMaxExperts];
+  __shared__ int32_t base[kMaxExperts];
+  __shared__ int32_t part[kRouteThreads];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kRouteThreads) base[e] = 0;
+  for (int c0 = 0; c0 < T; c0 += 64) {
+    const int ntok = min(64, T - c0);
+    for (int e = tid; e < E; e += kRouteThreads) mask[e] = 0ull;
+    __syncthreads();
+    for (int q = tid; q < ntok * k; q += kRouteThreads) {
+      const int e = min(max(idx[(int64_t)c0 * k + q], 0), E - 1);
+      atomicOr(&mask[e], 1ull << (q / k));
+    }
+    __syncthreads();
+    for (int q = tid; q < ntok * k; q += kRouteThreads) {
+      const int e = min(max(idx[(int64_t)c0 * k + q], 0), E - 1);
+      const int tl = q / k;
+      const unsigned long long below = tl ? (mask[e] & ((1ull << tl) - 1ull)) : 0ull;
+      inv[(int64_t)c0 * k + q] = base[e] + __popcll(below);  // rank inside the expert for now
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kRouteThreads) base[e] += __popcll(mask[e]);
+    __syncthreads();
+  }
+  // exclusive scan of base[0..E) -> offsets; each thread owns a contiguous run of experts
+  const int per = (E + kRouteThreads - 1) / kRouteThreads;
+  const int e0 = tid * per, e1 = min(E, e0 + per);
+  int run = 0;
+  for (int e = e0; e < e1; ++e) run += base[e];
+  part[tid] = run;
+  __syncthreads();
+  for (int off = 1; off < kRouteThreads; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int acc = part[tid] - run;  // exclusive prefix of this thread's run
+  for (int e = e0; e < e1; ++e) {
+    counts[e] = base[e];
+    offsets[e] = acc;
+    const int c = base[e];
+    base[e] = acc;  // reuse as the expert's first row
+    acc += c;
+  }
+  if (tid == kRouteThreads - 1) offsets[E] = part[kRouteThreads - 1];
+  __syncthreads();
+  for (int q = tid; q < T * k; q += kRouteThreads) {
+    const int e = min(max(idx[q], 0), E - 1);
+    const int row = base[e] + inv[q];
+    inv[q] = row;
+    perm[row] = q / k;
+  }
+}
+
+hipError_t launch_route(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* inv, hipStream_t s) {
+  if (E > kMaxExperts) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, idx, T, E, k, counts, offsets, perm, inv);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Combine + RMSNorm (eq. 11): u_t = sum_j p_tj O[inv[t, j]] in selection order, then
+// n_t = bf16(gamma * u_t / sqrt(mean(u_t^2) + eps)). One block per token.
+// ---------------------------------------------------------------------------------------------
+constexpr int kCombineThreads = 256;
+constexpr int kMaxWidth = 8192;
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ O,
+                                                                  const int32_t* __restrict__ inv,
+                                                                  const float* __restrict__ p, int k, int width,
+                                                                  const float* __restrict__ gamma, float eps, int mode,
+                                                                  u16* __restrict__ n_out, int64_t ldn,
+                                                                  float* __restrict__ u_out) {
+  __shared__ float us[kMaxWidth];
+  __shared__ int32_t rows[64];
+  __shared__ float pp[64];
+  __shared__ float red[kCombineThreads / 64];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < k) {
+    rows[tid] = inv[(int64_t)t * k + tid];
+    pp[tid] = p[(int64_t)t * k + tid];
+  }
+  __syncthreads();
+  float sq = 0.0f;
+  for (int c = 4 * tid; c < width; c += 4 * kCombineThreads) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int jj = 0; jj < k; ++jj) {
+      const float4 o = *(const float4*)(O + (int64_t)rows[jj] * width + c);
+      const float w = pp[jj];
+      a.x += w * o.x;
+      a.y += w * o.y;
+      a.z += w * o.z;
+      a.w += w * o.w;
+    }
+    *(float4*)(us + c) = a;
+    if (u_out) *(float4*)(u_out + (int64_t)t * width + c) = a;
+    sq += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+  }
+  if (mode != 0) return;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
+  if ((tid & 63) == 0) red[tid >> 6] = sq;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kCombineThreads / 64; ++i) tot += red[i];
+  const float rs = 1.0f / sqrtf(tot / (float)width + eps);
+  for (int c = tid; c < width; c += kCombineThreads)
+    n_out[(int64_t)t * ldn + c] = (u16)bf16_rne(gamma[c] * us[c] * rs);
+}
+
+hipError_t launch_combine(const float* O, const int32_t* inv, const float* p, int T, int k, int width,
+                          const float* gamma, float eps, int mode, uint16_t* n_out, int64_t ldn, float* u_out,
+                          hipStream_t s) {
+  if (width > kMaxWidth || k > 64 || width % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(kCombineThreads), 0, s, O, inv, p, k, width, gamma, eps, mode,
+                     n_out, ldn, u_out);
+  return hipGetLastError();
+}
+
+__global__ void f32_to_bf16_kernel(const float* __restrict__ in, u16* __restrict__ out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = (u16)bf16_rne(in[i]);
+}
+
+hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, in, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace k3

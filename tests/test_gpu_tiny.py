@@ -1,0 +1,166 @@
+"""GPU parity on the small layers: every intermediate of the HIP path against the fp64 oracle.
+
+Sizes: tiny LatentMoE (T = 64, d = 256, l = 128, hidden 96, E = 16, k = 4, one shared expert)
+and variants (MXFP8 activations, full-width conventional MoE, skewed bias with two shared
+experts); ragged token counts 1..63 cover partial 16-row tiles.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import layer, mx
+from tests import parity
+from tests.weightset import ArrayWeights
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, file=sys.__stderr__, flush=True)
+
+
+def _taps(shape, T, device="cuda"):
+    s = shape
+    le = s.expert_in
+    Tk = T * s.k
+    f8 = s.act == "mxfp8"
+    z = lambda *sh, dt: torch.zeros(*sh, dtype=dt, device=device)  # noqa: E731
+    t = dict(scores=z(T, s.E, dt=torch.float32), topk_idx=z(T, s.k, dt=torch.int32),
+             topk_p=z(T, s.k, dt=torch.float32), counts=z(s.E, dt=torch.int32), offsets=z(s.E + 1, dt=torch.int32),
+             perm=z(Tk, dt=torch.int32), inv=z(Tk, dt=torch.int32),
+             h=z(Tk, s.h, dt=torch.uint8 if f8 else torch.bfloat16), h_f32=z(Tk, s.h, dt=torch.float32),
+             expert_out=z(Tk, le, dt=torch.float32), u=z(T, le, dt=torch.float32))
+    if f8:
+        t["h_scales"] = z(Tk, s.h // 32, dt=torch.uint8)
+    if s.latent_moe:
+        t.update(z=z(T, s.l, dt=torch.uint8 if f8 else torch.bfloat16), z_f32=z(T, s.l, dt=torch.float32),
+                 n=z(T, s.l, dt=torch.bfloat16))
+        if f8:
+            t["z_scales"] = z(T, s.l // 32, dt=torch.uint8)
+    if s.Ns:
+        t["hs"] = z(T, s.Ns * s.hs, dt=torch.bfloat16)
+    return t
+
+
+def run_gpu(moe, wl, T):
+    x = workloads.device.x_tensor(wl, T)
+    taps = _taps(wl.shape, T)
+    y = moe.forward(x, taps=taps)
+    torch.cuda.synchronize()
+    out = {k: (parity.bf16_bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in taps.items()}
+    out["y"] = parity.np64(y)
+    return out
+
+
+_CASES = {}
+
+
+def case(name):
+    if name not in _CASES:
+        import workloads.device  # noqa: F401
+        wl = workloads.get(name)
+        w = ArrayWeights(wl)
+        _log(f"[case] {name}: packing")
+        moe = workloads.device.build_layer(w, wl.shape, max_tokens=wl.T)
+        _CASES[name] = (wl, w, moe)
+    return _CASES[name]
+
+
+def check_all(name, T):
+    wl, w, moe = case(name)
+    s = wl.shape
+    _log(f"[check] {name} T={T}")
+    g = run_gpu(moe, wl, T)
+    ref = layer.forward(wl.x_bits(T), w, s)
+    rt = ref.taps
+    # router: fp32 scores vs fp64
+    assert np.max(np.abs(g["scores"] - rt["scores"])) < 2e-6
+    flips = parity.check_routing(g, rt["selection"], s.E)
+    gidx = g["topk_idx"].astype(np.int64)
+    p_ref = layer.renorm(rt["scores"], gidx)
+    assert np.max(np.abs(g["topk_p"] - p_ref)) < 2e-6
+    if flips:
+        ref = layer.forward(wl.x_bits(T), w, s, select_override={t: gidx[t] for t in range(T)})
+        rt = ref.taps
+    f8 = s.act == "mxfp8"
+    # latent z at its quantisation point
+    if s.latent_moe:
+        if f8:
+            nz = parity.check_mx_quant(g["z"], g["z_scales"], g["z_f32"], rt["z"])
+        else:
+            nz = parity.check_bf16_quant(g["z"], g["z_f32"], rt["z"])
+        assert nz <= max(2, 1e-3 * g["z_f32"].size)
+    # GLU hidden (dispatched row order): strict quantisation of the GPU's own values, and the
+    # GPU pre-quantisation values close to the oracle's
+    if f8:
+        c2, s2 = mx.mx_quantize(g["h_f32"].astype(np.float64), "e4m3")
+        assert np.array_equal(c2, g["h"]) and np.array_equal(s2, g["h_scales"])
+    else:
+        assert np.array_equal(mx.bf16_round(g["h_f32"].astype(np.float64)), mx.bf16_from_bits(g["h"]))
+    rel_h = np.linalg.norm(g["h_f32"] - rt["hpre"]) / np.linalg.norm(rt["hpre"])
+    assert rel_h < (2e-2 if f8 else 2e-3), rel_h
+    rel_o = np.linalg.norm(g["expert_out"] - rt["expert_out"]) / np.linalg.norm(rt["expert_out"])
+    assert rel_o < (3e-2 if f8 else 5e-3), rel_o
+    parity.assert_y(g["u"], rt["u"], "u")
+    if s.latent_moe:
+        parity.assert_y(mx.bf16_from_bits(g["n"]), rt["n"], "n")
+    if s.Ns:
+        parity.assert_y(mx.bf16_from_bits(g["hs"]), np.concatenate(rt["hs"], axis=1), "shared hidden")
+    rel, ma = parity.assert_y(g["y"], ref.y)
+    _log(f"[check] {name} T={T}: flips {flips} rel_l2 {rel:.2e} maxabs/rms {ma:.2e}")
+    return g
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_mxfp8", "tiny_fullwidth", "tiny_skewed"])
+def test_full_parity(name):
+    check_all(name, workloads.get(name).T)
+
+
+@pytest.mark.parametrize("T", [1, 3, 16, 17, 40, 63])
+def test_ragged_token_counts(T):
+    check_all("tiny", T)
+
+
+def test_mxfp8_ragged():
+    check_all("tiny_mxfp8", 23)
+
+
+def test_deterministic_and_stream_order():
+    wl, w, moe = case("tiny")
+    x = workloads.device.x_tensor(wl)
+    y1 = moe.forward(x)
+    y2 = moe.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_identical_experts_gpu():
+    """All experts equal: the routed branch equals one expert's output regardless of routing."""
+    wl = workloads.get("tiny")
+    w = ArrayWeights(wl)
+    w.experts = [w.experts[2]] * wl.shape.E
+    moe = workloads.device.build_layer(w, wl.shape, max_tokens=wl.T)
+    g = run_gpu(moe, wl, wl.T)
+    ref = layer.forward(wl.x_bits(), w, wl.shape)
+    parity.assert_y(g["u"], ref.taps["u"], "u")
+    parity.assert_y(g["y"], ref.y)
+
+
+def test_t_zero_is_noop():
+    wl, w, moe = case("tiny")
+    x = torch.zeros(0, wl.shape.d, dtype=torch.bfloat16, device="cuda")
+    y = moe.forward(x)
+    assert y.shape == (0, wl.shape.d)
+
+
+def test_too_many_tokens_rejected():
+    wl, w, moe = case("tiny")
+    x = workloads.device.x_tensor(wl.with_tokens(wl.T + 1))
+    with pytest.raises(Exception) as ei:
+        moe.forward(x)
+    assert "max_tokens" in str(ei.value)

@@ -195,6 +195,13 @@ K3 = dict(d=7168, l=3584, h=3072, E=896, k=16, Ns=2, hs=3072)
 WORKLOADS = {
     "tiny": Workload("tiny", LayerShape(d=256, l=128, h=96, E=16, k=4, Ns=1, hs=96), T=64, seed=0,
                      note="tiny LatentMoE layer, CPU seconds"),
+    "tiny_mxfp8": Workload("tiny_mxfp8", LayerShape(d=256, l=128, h=96, E=16, k=4, Ns=1, hs=96, act="mxfp8"),
+                           T=64, seed=0, note="tiny layer, MXFP8 latent and hidden activations"),
+    "tiny_fullwidth": Workload("tiny_fullwidth", LayerShape(d=256, l=256, h=96, E=16, k=2, Ns=1, hs=96,
+                                                            latent_moe=0), T=64, seed=5,
+                               note="tiny conventional full-width MoE"),
+    "tiny_skewed": Workload("tiny_skewed", LayerShape(d=256, l=128, h=96, E=16, k=4, Ns=2, hs=64), T=96,
+                            seed=6, bias="zipf", zipf_alpha=0.3, note="tiny layer, Zipf-skewed bias, two shared"),
     "k3_decode_t64": Workload("k3_decode_t64", LayerShape(**K3), T=64, seed=1,
                               note="K3 shape decode, uniform routing (b = 0)"),
     "k3_decode_t512_zipf": Workload("k3_decode_t512_zipf", LayerShape(**K3), T=512, seed=1, bias="zipf",
