@@ -325,6 +325,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& args, const f32x4 (&acc
         ((float*)sg.out)[o] = 1.0f / (1.0f + expf(-v));
       } else if (mode == EPI_BF16) {
         ((u16*)sg.out)[o] = (u16)bf16_rne(v);
+        if (sg.pre) sg.pre[(int64_t)row * sg.ldpre + sg.col0 + col] = v;
       } else {  // EPI_BF16_ADD
         ((u16*)sg.out)[o] = (u16)bf16_rne(v + sg.addend[(int64_t)row * sg.ldadd + sg.col0 + col]);
       }
