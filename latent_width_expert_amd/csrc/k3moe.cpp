@@ -438,7 +438,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     }
     a.nseg = n;
     HIPCHECK(ctx, mark(ST_X, 0), "event");
-    HIPCHECK(ctx, launch_panel_gemm(a, 4, (int)ceil_div(T, 16), s), "x_gemm launch");
+    HIPCHECK(ctx, launch_panel_gemm(a, 4, (int)ceil_div(T, 16), GEMM_X, s), "x_gemm launch");
     HIPCHECK(ctx, mark(ST_X, 1), "event");
   }
   // ---- topk
@@ -485,7 +485,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     }
     a.nseg = 1;
     HIPCHECK(ctx, mark(ST_GATEUP, 0), "event");
-    HIPCHECK(ctx, launch_panel_gemm(a, 1, E, s), "gateup launch");
+    HIPCHECK(ctx, launch_panel_gemm(a, 1, E, GEMM_GATEUP, s), "gateup launch");
     HIPCHECK(ctx, mark(ST_GATEUP, 1), "event");
   }
   // ---- down
@@ -511,7 +511,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     sg.ldo = le;
     a.nseg = 1;
     HIPCHECK(ctx, mark(ST_DOWN, 0), "event");
-    HIPCHECK(ctx, launch_panel_gemm(a, 1, E, s), "down launch");
+    HIPCHECK(ctx, launch_panel_gemm(a, 1, E, GEMM_DOWN, s), "down launch");
     HIPCHECK(ctx, mark(ST_DOWN, 1), "event");
   }
   // ---- combine (+ RMSNorm)
@@ -546,7 +546,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     sg.addend = u;
     sg.ldadd = d;
     a.nseg = 1;
-    HIPCHECK(ctx, launch_panel_gemm(a, 4, (int)ceil_div(T, 16), s), "y_gemm launch");
+    HIPCHECK(ctx, launch_panel_gemm(a, 4, (int)ceil_div(T, 16), GEMM_Y, s), "y_gemm launch");
   } else {
     HIPCHECK(ctx, launch_f32_to_bf16(u, (uint16_t*)y_dev, (int64_t)T * d, s), "y convert launch");
   }

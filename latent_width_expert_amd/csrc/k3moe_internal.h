@@ -96,9 +96,11 @@ struct GemmArgs {
   EpiSeg seg[kMaxSeg];
 };
 
+enum GemmStage : int { GEMM_X = 0, GEMM_GATEUP = 1, GEMM_DOWN = 2, GEMM_Y = 3 };
+
 hipError_t launch_pack(const PackJob& job, hipStream_t s);
 // grouped (offsets != null): grid.y = n_groups; dense: grid.y = ceil(M / 16)
-hipError_t launch_panel_gemm(const GemmArgs& a, int ksplit, int grid_y, hipStream_t s);
+hipError_t launch_panel_gemm(const GemmArgs& a, int ksplit, int grid_y, GemmStage stage, hipStream_t s);
 hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* idx, float* p,
                        hipStream_t s);
 hipError_t launch_route(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,

@@ -333,7 +333,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& args, const f32x4 (&acc
   }
 }
 
-template <int KSPLIT, int AFMT, int NBUF>
+// TAG only separates the stages (x_gemm, gateup, down, y_gemm) into distinct kernel symbols.
+template <int KSPLIT, int AFMT, int NBUF, int TAG>
 __global__ __launch_bounds__(256) void panel_gemm_kernel(GemmArgs args) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -415,25 +416,39 @@ __global__ __launch_bounds__(256) void panel_gemm_kernel(GemmArgs args) {
   }
 }
 
-hipError_t launch_panel_gemm(const GemmArgs& a, int ksplit, int grid_y, hipStream_t s) {
-  if (grid_y <= 0 || a.P <= 0) return hipSuccess;
+template <int TAG>
+static hipError_t launch_tagged(const GemmArgs& a, int ksplit, int grid_y, hipStream_t s) {
   constexpr int NB = 3;
   if (ksplit == 1) {
     dim3 grid((unsigned)ceil_div(a.P, 4), (unsigned)grid_y);
     if (a.a_fmt == A_BF16)
-      hipLaunchKernelGGL((panel_gemm_kernel<1, A_BF16, NB>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((panel_gemm_kernel<1, A_BF16, NB, TAG>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((panel_gemm_kernel<1, A_MXFP8, NB>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((panel_gemm_kernel<1, A_MXFP8, NB, TAG>), grid, dim3(256), 0, s, a);
   } else if (ksplit == 4) {
     dim3 grid((unsigned)a.P, (unsigned)grid_y);
     if (a.a_fmt == A_BF16)
-      hipLaunchKernelGGL((panel_gemm_kernel<4, A_BF16, NB>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((panel_gemm_kernel<4, A_BF16, NB, TAG>), grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((panel_gemm_kernel<4, A_MXFP8, NB>), grid, dim3(256), 0, s, a);
+      return hipErrorInvalidValue;
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_panel_gemm(const GemmArgs& a, int ksplit, int grid_y, GemmStage stage, hipStream_t s) {
+  if (grid_y <= 0 || a.P <= 0) return hipSuccess;
+  switch (stage) {
+    case GEMM_X:
+      return launch_tagged<GEMM_X>(a, ksplit, grid_y, s);
+    case GEMM_GATEUP:
+      return launch_tagged<GEMM_GATEUP>(a, ksplit, grid_y, s);
+    case GEMM_DOWN:
+      return launch_tagged<GEMM_DOWN>(a, ksplit, grid_y, s);
+    default:
+      return launch_tagged<GEMM_Y>(a, ksplit, grid_y, s);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
