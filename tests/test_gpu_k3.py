@@ -1,0 +1,160 @@
+"""GPU parity at K3 shape (d = 7168, l = 3584, hidden 3072, E = 896, k = 16, two shared experts), in
+the launch configuration the benchmark times.
+
+Every token: router scores, selection (exact up to oracle key ties < 1e-6, counted), p, counts,
+offsets, permutation and inverse (bit-exact), and the latent z at its quantisation point (bf16
+or MXFP8 codes: strict against the oracle's encoder on the GPU's fp32 values, end to end
+against the oracle's own values). Sampled tokens: y, u, n and the shared hidden against the
+oracle's per-token forward. One packed layer is resident at a time.
+"""
+from __future__ import annotations
+
+import gc
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+import workloads.device as wdev
+from oracle import layer, mx
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, file=sys.__stderr__, flush=True)
+
+
+_CUR = {"key": None, "moe": None}
+
+
+def get_layer(wl, max_tokens):
+    """Packed layer for the workload's seed, shape and activation format (bias re-packed)."""
+    key = (wl.seed, wl.shape, max_tokens)
+    if _CUR["key"] != key:
+        _CUR["moe"] = None
+        gc.collect()
+        torch.cuda.empty_cache()
+        _log(f"[k3] packing seed {wl.seed} {wl.shape}")
+        _CUR["moe"] = wdev.build_layer(wl, wl.shape, max_tokens=max_tokens, verbose=True)
+        _CUR["key"] = key
+        _CUR["bias"] = wl.bias, wl.zipf_alpha
+    if _CUR.get("bias") != (wl.bias, wl.zipf_alpha):
+        _CUR["moe"].pack(dense=wdev.upload_dense(wl, wl.shape))
+        torch.cuda.synchronize()
+        _CUR["bias"] = wl.bias, wl.zipf_alpha
+    return _CUR["moe"]
+
+
+def run_taps(moe, wl, T):
+    s = wl.shape
+    f8 = s.act == "mxfp8"
+    dev = "cuda"
+    t = dict(scores=torch.empty(T, s.E, dtype=torch.float32, device=dev),
+             topk_idx=torch.empty(T, s.k, dtype=torch.int32, device=dev),
+             topk_p=torch.empty(T, s.k, dtype=torch.float32, device=dev),
+             counts=torch.empty(s.E, dtype=torch.int32, device=dev),
+             offsets=torch.empty(s.E + 1, dtype=torch.int32, device=dev),
+             perm=torch.empty(T * s.k, dtype=torch.int32, device=dev),
+             inv=torch.empty(T * s.k, dtype=torch.int32, device=dev),
+             u=torch.empty(T, s.expert_in, dtype=torch.float32, device=dev))
+    if s.latent_moe:
+        t.update(z=torch.empty(T, s.l, dtype=torch.uint8 if f8 else torch.bfloat16, device=dev),
+                 z_f32=torch.empty(T, s.l, dtype=torch.float32, device=dev),
+                 n=torch.empty(T, s.l, dtype=torch.bfloat16, device=dev))
+        if f8:
+            t["z_scales"] = torch.empty(T, s.l // 32, dtype=torch.uint8, device=dev)
+    if s.Ns:
+        t["hs"] = torch.empty(T, s.Ns * s.hs, dtype=torch.bfloat16, device=dev)
+    x = wdev.x_tensor(wl, T)
+    y = moe.forward(x, taps=t)
+    torch.cuda.synchronize()
+    g = {k: (parity.bf16_bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in t.items()}
+    g["y"] = parity.np64(y)
+    return g
+
+
+def check_layer(wl, sample, max_tokens=None):
+    s = wl.shape
+    T = wl.T
+    moe = get_layer(wl, max_tokens or T)
+    _log(f"[k3] {wl.name}: GPU forward T={T}")
+    g = run_taps(moe, wl, T)
+    xb = wl.x_bits()
+    xh = mx.bf16_from_bits(xb)
+    # router over every token
+    sc = layer.router_scores(xh, layer.dequant(wl.w_router()))
+    assert np.max(np.abs(g["scores"] - sc)) < 1e-5
+    sel = layer.select_topk(sc, wl.router_bias(), s.k)
+    flips = parity.check_routing(g, sel, s.E)
+    gidx = g["topk_idx"].astype(np.int64)
+    assert np.max(np.abs(g["topk_p"] - layer.renorm(sc, gidx))) < 1e-5
+    counts = g["counts"]
+    _log(f"[k3] {wl.name}: routing ok, flips {flips}, active experts {(counts > 0).sum()}, "
+         f"max/mean load {counts.max() / counts.mean():.2f}")
+    # latent z of every token at its quantisation point
+    if s.latent_moe:
+        Wd = layer.dequant(wl.w_down())
+        nz = 0
+        for r0 in range(0, T, 1024):
+            z = xh[r0:r0 + 1024] @ Wd.T
+            if s.act == "mxfp8":
+                nz += parity.check_mx_quant(g["z"][r0:r0 + 1024], g["z_scales"][r0:r0 + 1024],
+                                            g["z_f32"][r0:r0 + 1024], z)
+            else:
+                nz += parity.check_bf16_quant(g["z"][r0:r0 + 1024], g["z_f32"][r0:r0 + 1024], z)
+        assert nz <= 1e-4 * T * s.l + 2
+        _log(f"[k3] {wl.name}: z quantisation ok ({nz} boundary cases)")
+    # sampled tokens through the whole layer
+    ov = {i: gidx[t] for i, t in enumerate(sample)}
+    ref = layer.forward(xb[sample], wl, s, select_override=ov, keep_expert_rows=False)
+    rel, ma = parity.assert_y(g["y"][sample], ref.y, "y")
+    parity.assert_y(g["u"][sample], ref.taps["u"], "u")
+    if s.latent_moe:
+        parity.assert_y(mx.bf16_from_bits(g["n"][sample]), ref.taps["n"], "n")
+    if s.Ns:
+        parity.assert_y(mx.bf16_from_bits(g["hs"][sample]), np.concatenate(ref.taps["hs"], axis=1), "shared")
+    _log(f"[k3] {wl.name}: sampled tokens {list(sample)}: y rel L2 {rel:.2e}, max-abs/rms {ma:.2e}")
+    return g
+
+
+@pytest.mark.timeout(900)
+def test_k3_decode_t64():
+    check_layer(workloads.get("k3_decode_t64"), [0, 21, 63], max_tokens=512)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["k3_decode_t512_zipf", "k3_decode_t512_zipf_cal"])
+def test_k3_decode_t512_skewed(name):
+    g = check_layer(workloads.get(name), [5, 511], max_tokens=512)
+    c = g["counts"]
+    assert c.sum() == 512 * 16
+
+
+@pytest.mark.timeout(900)
+def test_k3_prefill_t8192_mxfp8():
+    check_layer(workloads.get("k3_prefill_t8192"), [0, 8191])
+
+
+@pytest.mark.timeout(900)
+def test_k3_decode_repeat_bit_identical():
+    """Determinism at K3 shape: two forwards give identical y and permutation."""
+    wl = workloads.get("k3_prefill_t8192").with_tokens(1024)
+    moe = get_layer(workloads.get("k3_prefill_t8192"), 8192)
+    x = wdev.x_tensor(wl)
+    perm = [torch.empty(1024 * 16, dtype=torch.int32, device="cuda") for _ in range(2)]
+    y1 = moe.forward(x, taps={"perm": perm[0]})
+    y2 = moe.forward(x, taps={"perm": perm[1]})
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(perm[0], perm[1])
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [64, 2048])
+def test_fullwidth(T):
+    wl = workloads.get("fullwidth_t2048").with_tokens(T)
+    check_layer(wl, [0, T - 1], max_tokens=2048)
