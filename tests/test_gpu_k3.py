@@ -98,15 +98,18 @@ def check_layer(wl, sample, max_tokens=None):
     # latent z of every token at its quantisation point
     if s.latent_moe:
         Wd = layer.dequant(wl.w_down())
+        aWd = np.abs(Wd)
         nz = 0
         for r0 in range(0, T, 1024):
-            z = xh[r0:r0 + 1024] @ Wd.T
+            xs = xh[r0:r0 + 1024]
+            z = xs @ Wd.T
+            bound = parity.dot_error_bound(np.abs(xs), aWd)
             if s.act == "mxfp8":
                 nz += parity.check_mx_quant(g["z"][r0:r0 + 1024], g["z_scales"][r0:r0 + 1024],
-                                            g["z_f32"][r0:r0 + 1024], z)
+                                            g["z_f32"][r0:r0 + 1024], z, bound)
             else:
-                nz += parity.check_bf16_quant(g["z"][r0:r0 + 1024], g["z_f32"][r0:r0 + 1024], z)
-        assert nz <= 1e-4 * T * s.l + 2
+                nz += parity.check_bf16_quant(g["z"][r0:r0 + 1024], g["z_f32"][r0:r0 + 1024], z, bound)
+        assert nz <= 1e-3 * T * s.l + 2
         _log(f"[k3] {wl.name}: z quantisation ok ({nz} boundary cases)")
     # sampled tokens through the whole layer
     ov = {i: gidx[t] for i, t in enumerate(sample)}

@@ -90,10 +90,12 @@ def check_all(name, T):
     f8 = s.act == "mxfp8"
     # latent z at its quantisation point
     if s.latent_moe:
+        xh = mx.bf16_from_bits(wl.x_bits(T))
+        bound = parity.dot_error_bound(np.abs(xh), np.abs(layer.dequant(w.w_down())))
         if f8:
-            nz = parity.check_mx_quant(g["z"], g["z_scales"], g["z_f32"], rt["z"])
+            nz = parity.check_mx_quant(g["z"], g["z_scales"], g["z_f32"], rt["z"], bound)
         else:
-            nz = parity.check_bf16_quant(g["z"], g["z_f32"], rt["z"])
+            nz = parity.check_bf16_quant(g["z"], g["z_f32"], rt["z"], bound)
         assert nz <= max(2, 1e-3 * g["z_f32"].size)
     # GLU hidden (dispatched row order): strict quantisation of the GPU's own values, and the
     # GPU pre-quantisation values close to the oracle's
