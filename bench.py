@@ -30,6 +30,21 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes recorded in
+    profiles/, or None when the kernel source changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    src = os.path.join(ROOT, "latent_width_expert_amd", "csrc", "kernels.hip")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernels_hip_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k["hbm_bytes_per_launch"]
+
+
 def mxfp4_bytes(n_elems: int) -> int:
     return n_elems // 2 + n_elems // 32
 
@@ -135,7 +150,8 @@ def main():
                    "latent_moe": s.latent_moe, "weights": "MXFP4", "parallelism": "single GPU"},
         "roofline": {"kernel": "gateup (grouped GLU gate/up GEMM, MXFP4 weight stream)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": gu_alg, "avg_launch_ms": gu_ms},
+                     "traffic": recorded_traffic(wl.name, "gateup"), "algorithmic_bytes_per_launch": gu_alg,
+                     "avg_launch_ms": gu_ms},
         "layer_hbm_gbps": layer_alg / (ms_step * 1e-3) / 1e9,
         "layer_algorithmic_bytes": layer_alg,
         "layer_tflops": flops_tok * T / (ms_step * 1e-3) / 1e12,

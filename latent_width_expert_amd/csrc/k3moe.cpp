@@ -16,6 +16,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -113,6 +114,13 @@ int k3moe_create(const k3moe_config* cfg, k3moe_ctx** out) {
   if ((int64_t)c.max_tokens * c.top_k > (int64_t)1 << 30)
     return fail(nullptr, K3MOE_ETOOBIG, "max_tokens * top_k too large");
   if (le > 8192) return fail(nullptr, K3MOE_EUNSUPPORTED, "expert width above 8192");
+  {
+    // every GEMM operand must stay addressable by a 32-bit buffer offset
+    const int64_t T = c.max_tokens, lim = ((int64_t)1 << 31) - ((int64_t)1 << 25);
+    const int64_t yk = (c.latent_moe ? le : 0) + (int64_t)c.n_shared * c.shared_hidden;
+    const int64_t worst = std::max({T * c.d_model * 2, T * c.top_k * c.hidden * 2, T * yk * 2, T * le * 2});
+    if (worst > lim) return fail(nullptr, K3MOE_ETOOBIG, "max_tokens too large: an operand exceeds 2 GiB");
+  }
   if (!(c.rms_eps >= 0.0f)) return fail(nullptr, K3MOE_EINVAL, "rms_eps must be >= 0");
 
   k3moe_ctx* x = new k3moe_ctx();
@@ -402,6 +410,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     a.a_fmt = A_BF16;
     a.A = x_dev;
     a.lda = d;
+    a.a_bytes = (int64_t)T * d * 2;
     a.M = T;
     int n = 0;
     EpiSeg& r = a.seg[n++];
@@ -438,7 +447,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     }
     a.nseg = n;
     HIPCHECK(ctx, mark(ST_X, 0), "event");
-    HIPCHECK(ctx, launch_panel_gemm(a, 4, (int)ceil_div(T, 16), GEMM_X, s), "x_gemm launch");
+    HIPCHECK(ctx, launch_panel_gemm(a, GEMM_X, s), "x_gemm launch");
     HIPCHECK(ctx, mark(ST_X, 1), "event");
   }
   // ---- topk
@@ -461,15 +470,19 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
       a.a_fmt = f8 ? A_MXFP8 : A_BF16;
       a.A = z;
       a.lda = l;
+      a.a_bytes = (int64_t)T * l * (f8 ? 1 : 2);
       a.A_scales = zs;
       a.ldas = l / 32;
+      a.as_bytes = (int64_t)T * (l / 32);
     } else {
       a.a_fmt = A_BF16;
       a.A = x_dev;
       a.lda = d;
+      a.a_bytes = (int64_t)T * d * 2;
     }
     a.rowmap = perm;
     a.offsets = offsets;
+    a.n_groups = E;
     EpiSeg& sg = a.seg[0];
     sg.p0 = 0;
     sg.p1 = ctx->gu_P;
@@ -485,7 +498,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     }
     a.nseg = 1;
     HIPCHECK(ctx, mark(ST_GATEUP, 0), "event");
-    HIPCHECK(ctx, launch_panel_gemm(a, 1, E, GEMM_GATEUP, s), "gateup launch");
+    HIPCHECK(ctx, launch_panel_gemm(a, GEMM_GATEUP, s), "gateup launch");
     HIPCHECK(ctx, mark(ST_GATEUP, 1), "event");
   }
   // ---- down
@@ -499,9 +512,12 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     a.a_fmt = f8 ? A_MXFP8 : A_BF16;
     a.A = H;
     a.lda = h;
+    a.a_bytes = (int64_t)T * k * h * (f8 ? 1 : 2);
     a.A_scales = Hs;
     a.ldas = h / 32;
+    a.as_bytes = (int64_t)T * k * (h / 32);
     a.offsets = offsets;
+    a.n_groups = E;
     EpiSeg& sg = a.seg[0];
     sg.p0 = 0;
     sg.p1 = ctx->dn_P;
@@ -511,7 +527,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     sg.ldo = le;
     a.nseg = 1;
     HIPCHECK(ctx, mark(ST_DOWN, 0), "event");
-    HIPCHECK(ctx, launch_panel_gemm(a, 1, E, GEMM_DOWN, s), "down launch");
+    HIPCHECK(ctx, launch_panel_gemm(a, GEMM_DOWN, s), "down launch");
     HIPCHECK(ctx, mark(ST_DOWN, 1), "event");
   }
   // ---- combine (+ RMSNorm)
@@ -535,6 +551,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     a.a_fmt = A_BF16;
     a.A = abuf;
     a.lda = ctx->y_K;
+    a.a_bytes = (int64_t)T * ctx->y_K * 2;
     a.M = T;
     EpiSeg& sg = a.seg[0];
     sg.p0 = 0;
@@ -546,7 +563,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     sg.addend = u;
     sg.ldadd = d;
     a.nseg = 1;
-    HIPCHECK(ctx, launch_panel_gemm(a, 4, (int)ceil_div(T, 16), GEMM_Y, s), "y_gemm launch");
+    HIPCHECK(ctx, launch_panel_gemm(a, GEMM_Y, s), "y_gemm launch");
   } else {
     HIPCHECK(ctx, launch_f32_to_bf16(u, (uint16_t*)y_dev, (int64_t)T * d, s), "y convert launch");
   }

@@ -87,11 +87,15 @@ struct GemmArgs {
   int32_t a_fmt;           // AFmt
   const void* A;           // bf16 or E4M3 codes, row-major, leading dimension lda (elements)
   int64_t lda;
+  int64_t a_bytes;         // bytes of A (loads past it read zeros); below 2^31 - 2^24
   const uint8_t* A_scales; // MXFP8: E8M0 bytes, leading dimension ldas
   int64_t ldas;
+  int64_t as_bytes;        // bytes of A_scales
   const int32_t* rowmap;   // optional: output row -> A row
   const int32_t* offsets;  // grouped: rows of group g are [offsets[g], offsets[g+1])
+  int32_t n_groups;        // grouped: number of groups
   int32_t M;               // dense: rows
+  int32_t m_passes;        // dense: row passes (set by the launcher)
   int32_t nseg;
   EpiSeg seg[kMaxSeg];
 };
@@ -99,8 +103,8 @@ struct GemmArgs {
 enum GemmStage : int { GEMM_X = 0, GEMM_GATEUP = 1, GEMM_DOWN = 2, GEMM_Y = 3 };
 
 hipError_t launch_pack(const PackJob& job, hipStream_t s);
-// grouped (offsets != null): grid.y = n_groups; dense: grid.y = ceil(M / 16)
-hipError_t launch_panel_gemm(const GemmArgs& a, int ksplit, int grid_y, GemmStage stage, hipStream_t s);
+// Grouped launches (offsets != null) use n_groups blocks along y; dense launches cover M rows.
+hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s);
 hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* idx, float* p,
                        hipStream_t s);
 hipError_t launch_route(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,

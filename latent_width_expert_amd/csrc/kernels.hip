@@ -58,6 +58,18 @@ __device__ __forceinline__ int mx_shared_exp(float amax, int emax) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// Raw buffer loads: the hardware bounds-checks every load against the resource's byte count and
+// returns zeros for out-of-range offsets without touching memory, so tails and masked lanes need
+// no branches (and the wait counters stay exact).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kOOB = 0x7F000000;        // an offset past every resource (resources stay below it)
+constexpr int kNT = 2;                  // non-temporal cache policy
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Packer: canonical MXFP4 -> panels. One thread per (panel, window, lane).
 // ---------------------------------------------------------------------------------------------
@@ -110,15 +122,18 @@ hipError_t launch_pack(const PackJob& job, hipStream_t s) {
 // ---------------------------------------------------------------------------------------------
 // Panel GEMM.
 //
-// One wave computes one panel (64 weight rows) for a 16-row tile of A over its share of the
-// windows. Per window it loads the 4 KB of codes and 256 B of scales of the panel (5 coalesced
-// loads per lane) and the lane's 32 A values, converts the E2M1 codes to bf16 with their E8M0
-// scale (v_cvt_scalef32_pk_bf16_fp4, exact) and issues 16 MFMA 16x16x32 bf16. Loads run
-// NBUF - 1 windows ahead in a register ring, so each wave keeps several KB in flight.
+// One wave computes one panel (64 weight rows) for MT 16-row tiles of A over its share of the
+// windows. Per window it loads the 4 KB of codes and 256 B of scales of the panel (5 coalesced,
+// non-temporal loads per lane: the weights are streamed once and should not displace the
+// activations in L2) and the lane's 32 A values per tile, converts the E2M1 codes to bf16 with
+// their E8M0 scale (v_cvt_scalef32_pk_bf16_fp4, exact) and issues 16 MT MFMA 16x16x32 bf16 (each
+// weight operand is converted once and reused for the MT tiles). Loads run NBUF - 1 windows
+// ahead in a register ring, so each wave keeps several KB in flight.
 // MFMA lane roles: A lane (i = l % 16, g = l / 16) supplies row i, B lane (j, g) weight row j;
 // both take K elements [32 (4w + g) + 8 s, +8) in MFMA step s of window w; D lane (j, g) ends
 // with rows 4 g + r (r = 0..3), column j.
-// KSPLIT > 1: the four waves of a block split the windows of one panel and reduce through LDS.
+// KSPLIT > 1: KSPLIT waves of a block split the windows of one panel and reduce through LDS in
+// a fixed tree order (deterministic).
 // ---------------------------------------------------------------------------------------------
 template <int AFMT>
 struct AWin;
@@ -137,54 +152,46 @@ struct WWin {
   u32 sc;
 };
 
-struct WinBuf_bf16 {
-  WWin w;
-  AWin<A_BF16> a;
-};
-
-template <int AFMT>
+template <int AFMT, int MT>
 struct WinBuf {
   WWin w;
-  AWin<AFMT> a;
+  AWin<AFMT> a[MT];
 };
 
-// codes: panel base + lane * 16; scales: panel base + 4096 + lane * 4
-__device__ __forceinline__ void load_w(WWin& b, const uint8_t* pcode, const uint8_t* pscale, int w) {
-  const int64_t off = (int64_t)w * kPanelWinBytes;
+template <int AFMT, int MT>
+struct ATile {
+  AWin<AFMT> a[MT];
+};
+
+// One panel-window of the wave's window range (window wi relative to the range start).
+__device__ __forceinline__ void load_w(WWin& b, rsrc_t wr, int lane, int wi) {
+  const int off = wi * kPanelWinBytes;
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) b.c[rt] = *(const u32x4*)(pcode + off + rt * 1024);
-  b.sc = *(const u32*)(pscale + off);
+  for (int rt = 0; rt < 4; ++rt) b.c[rt] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + rt * 1024 + lane * 16, 0, kNT);
+  b.sc = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 4096 + lane * 4, 0, kNT);
 }
 
+// The lane's MX block (K block kb) of A row arow; invalid lanes and blocks past K read zeros.
 template <int AFMT>
-__device__ __forceinline__ void load_a(AWin<AFMT>& a, const GemmArgs& args, int64_t arow, bool valid, int kb);
+__device__ __forceinline__ void load_a(AWin<AFMT>& a, rsrc_t ar, rsrc_t asr, const GemmArgs& args, int arow,
+                                       bool valid, int kb);
 
 template <>
-__device__ __forceinline__ void load_a<A_BF16>(AWin<A_BF16>& a, const GemmArgs& args, int64_t arow, bool valid,
-                                               int kb) {
-  if (valid && kb * 32 < args.K) {
-    const u32x4* p = (const u32x4*)((const u16*)args.A + arow * args.lda + kb * 32);
+__device__ __forceinline__ void load_a<A_BF16>(AWin<A_BF16>& a, rsrc_t ar, rsrc_t, const GemmArgs& args, int arow,
+                                               bool valid, int kb) {
+  const int off = (valid && kb * 32 < args.K) ? (arow * (int)args.lda + kb * 32) * 2 : kOOB;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) a.v[s] = p[s];
-  } else {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) a.v[s] = u32x4{0u, 0u, 0u, 0u};
-  }
+  for (int s = 0; s < 4; ++s) a.v[s] = __builtin_amdgcn_raw_buffer_load_b128(ar, off + 16 * s, 0, 0);
 }
 
 template <>
-__device__ __forceinline__ void load_a<A_MXFP8>(AWin<A_MXFP8>& a, const GemmArgs& args, int64_t arow, bool valid,
-                                                int kb) {
-  if (valid && kb * 32 < args.K) {
-    const u32x4* p = (const u32x4*)((const uint8_t*)args.A + arow * args.lda + kb * 32);
-    a.v[0] = p[0];
-    a.v[1] = p[1];
-    a.sc = args.A_scales[arow * args.ldas + kb];
-  } else {
-    a.v[0] = u32x4{0u, 0u, 0u, 0u};
-    a.v[1] = u32x4{0u, 0u, 0u, 0u};
-    a.sc = 127;
-  }
+__device__ __forceinline__ void load_a<A_MXFP8>(AWin<A_MXFP8>& a, rsrc_t ar, rsrc_t asr, const GemmArgs& args,
+                                                int arow, bool valid, int kb) {
+  const bool in = valid && kb * 32 < args.K;
+  const int off = in ? arow * (int)args.lda + kb * 32 : kOOB;
+  a.v[0] = __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0);
+  a.v[1] = __builtin_amdgcn_raw_buffer_load_b128(ar, off + 16, 0, 0);
+  a.sc = __builtin_amdgcn_raw_buffer_load_b8(asr, in ? arow * (int)args.ldas + kb : kOOB, 0, 0);
 }
 
 // bf16 operand of MFMA step s (K elements 8 s .. 8 s + 7 of the lane's block)
@@ -218,18 +225,19 @@ __device__ __forceinline__ bf16x8 fp4_operand(u32 d, float sc) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-template <int AFMT>
-__device__ __forceinline__ void compute_window(f32x4 (&acc)[4], const WWin& w, const AWin<AFMT>& a) {
-  bf16x8 av[4];
+template <int AFMT, int MT>
+__device__ __forceinline__ void compute_window(f32x4 (&acc)[MT][4], const WWin& w, const AWin<AFMT> (&a)[MT]) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) av[s] = a_operand<AFMT>(a, s);
+  for (int s = 0; s < 4; ++s) {
+    bf16x8 av[MT];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const float sc = e8m0_f32((w.sc >> (8 * rt)) & 0xFFu);
+    for (int mt = 0; mt < MT; ++mt) av[mt] = a_operand<AFMT>(a[mt], s);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 b = fp4_operand(w.c[rt][s], sc);
-      acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[s], b, acc[rt], 0, 0, 0);
+    for (int rt = 0; rt < 4; ++rt) {
+      const bf16x8 wv = fp4_operand(w.c[rt][s], e8m0_f32((w.sc >> (8 * rt)) & 0xFFu));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], wv, acc[mt][rt], 0, 0, 0);
     }
   }
 }
@@ -253,6 +261,7 @@ __device__ __forceinline__ void mxfp8_block(float v0, float v1, u32& c0, u32& c1
   c1 = e4m3_code(v1 * inv);
 }
 
+// Epilogue of one 16-row tile (rows mb .. mb + 15, valid below r1) of one panel.
 __device__ __forceinline__ void epilogue(const GemmArgs& args, const f32x4 (&acc)[4], int panel, int mb, int r1,
                                          int lane) {
   int si = 0;
@@ -264,19 +273,19 @@ __device__ __forceinline__ void epilogue(const GemmArgs& args, const f32x4 (&acc
   const int mode = sg.mode;
   if (mode == EPI_SWIGLU_BF16 || mode == EPI_SWIGLU_MXFP8 || mode == EPI_MXFP8) {
     const bool glu = mode != EPI_MXFP8;
+    const int nblk = glu ? 1 : 2;  // 32-wide blocks per panel: GLU 32 units, plain 64 columns
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = mb + 4 * gq + r;
       const bool ok = row < r1;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        // block q of the panel: 32 columns (GLU: 32 units over both pairs of row-tiles)
+        if (q >= nblk) break;  // uniform; static indices keep acc in registers
         float v0, v1;
-        int c0i, c1i;  // column of v0, v1 within the segment
+        int c0i, c1i;  // columns of v0, v1 within the segment
         if (glu) {
-          v0 = silu(acc[0][r]) * acc[1][r];  // q selects the pair below
-          v1 = silu(acc[2][r]) * acc[3][r];
-          if (q == 1) break;                  // both unit halves handled in q == 0
+          v0 = silu(acc[0][r]) * acc[1][r];  // unit 32 pl + j
+          v1 = silu(acc[2][r]) * acc[3][r];  // unit 32 pl + 16 + j
           c0i = 32 * pl + j;
           c1i = 32 * pl + 16 + j;
         } else {
@@ -333,129 +342,214 @@ __device__ __forceinline__ void epilogue(const GemmArgs& args, const f32x4 (&acc
   }
 }
 
-// TAG only separates the stages (x_gemm, gateup, down, y_gemm) into distinct kernel symbols.
-template <int KSPLIT, int AFMT, int NBUF, int TAG>
-__global__ __launch_bounds__(256) void panel_gemm_kernel(GemmArgs args) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  constexpr int PPB = 4 / KSPLIT;
-  const int panel = blockIdx.x * PPB + wave / KSPLIT;
-  const int ks = wave % KSPLIT;
-  const bool panel_ok = panel < args.P;
+// Waves per block: KSPLIT waves per panel, 4 panels per block when KSPLIT == 1.
+template <int KSPLIT>
+struct BlockShape {
+  static constexpr int waves = KSPLIT == 1 ? 4 : KSPLIT;
+  static constexpr int panels = KSPLIT == 1 ? 4 : 1;
+};
 
-  int grp = 0, r0, r1;
+// TAG only separates the stages (x_gemm, gateup, down, y_gemm) into distinct kernel symbols.
+// AHEAD: A tiles travel in the weight ring (prefetched NBUF - 1 windows ahead, few rows per
+// wave); otherwise each window's A tile is loaded just before the next weight prefetch (MT
+// tiles of A would not fit the ring), so waiting for it never waits for that prefetch.
+template <int KSPLIT, int AFMT, int NBUF, int MT, bool AHEAD, int TAG>
+__global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_kernel(GemmArgs args) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps the resources scalar
+  int pblock, grp = 0, r0, r1;
   if (args.offsets) {
+    pblock = blockIdx.x;
     grp = blockIdx.y;
     r0 = args.offsets[grp];
     r1 = args.offsets[grp + 1];
   } else {
-    r0 = blockIdx.y * 16;
-    r1 = min(r0 + 16, args.M);
+    // Dense: the M passes of one panel block are placed on block ids b = 32 q + 8 m + r (pass m,
+    // panel block 8 q + r). Blocks are dealt to the 8 XCDs round robin, so the passes of a panel
+    // run on the same XCD one after another and re-read its weights from that XCD's L2.
+    const int b = blockIdx.x;
+    const int per = 8 * args.m_passes;
+    const int m = (b % per) / 8;
+    pblock = (b / per) * 8 + b % 8;
+    r0 = m * 16 * MT;
+    r1 = min(r0 + 16 * MT, args.M);
   }
-  if (r0 >= r1) return;  // uniform over the block
+  const int panel = pblock * BlockShape<KSPLIT>::panels + wave / KSPLIT;
+  const int ks = wave % KSPLIT;
+  const bool panel_ok = panel < args.P;
+  if (r0 >= r1 || pblock * BlockShape<KSPLIT>::panels >= args.P) return;  // uniform over the block
 
   const int wbeg = (args.wwin * ks) / KSPLIT;
   const int wend = (args.wwin * (ks + 1)) / KSPLIT;
-  const uint8_t* pbase = args.W + (int64_t)grp * args.w_group_stride +
-                         (int64_t)(panel_ok ? panel : 0) * args.wwin * kPanelWinBytes;
-  const uint8_t* pcode = pbase + lane * 16;
-  const uint8_t* pscale = pbase + 4096 + lane * 4;
+  const int nwin = panel_ok ? wend - wbeg : 0;
+  const rsrc_t wr = make_rsrc(args.W + (int64_t)grp * args.w_group_stride +
+                                  ((int64_t)(panel_ok ? panel : 0) * args.wwin + wbeg) * kPanelWinBytes,
+                              (int64_t)nwin * kPanelWinBytes);
+  const rsrc_t ar = make_rsrc(args.A, args.a_bytes);
+  const rsrc_t asr = make_rsrc(args.A_scales, args.A_scales ? args.as_bytes : 0);
   const int g = lane >> 4;
 
-  __shared__ f32x4 red[KSPLIT > 1 ? (KSPLIT - 1) * 4 * 64 : 1];
+  // partial sums of the upper half of the K-split waves, per tree level
+  __shared__ f32x4 red[KSPLIT > 1 ? (KSPLIT / 2) * MT * 4 * 64 : 1];
 
-  for (int mb = r0; mb < r1; mb += 16) {
-    const int row = mb + (lane & 15);
-    const bool rv = row < r1;
-    const int64_t arow = rv ? (args.rowmap ? (int64_t)args.rowmap[row] : (int64_t)row) : 0;
-
-    f32x4 acc[4];
+  for (int mb = r0; mb < r1; mb += 16 * MT) {
+    bool rv[MT];
+    int arow[MT];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = mb + 16 * mt + (lane & 15);
+      rv[mt] = row < r1;
+      arow[mt] = rv[mt] ? (args.rowmap ? args.rowmap[row] : row) : 0;
+    }
 
-    if (panel_ok && wbeg < wend) {
-      WinBuf<AFMT> buf[NBUF];
+    f32x4 acc[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Loads are issued unconditionally: past the range they return zeros without memory traffic.
+    auto load_tile = [&](AWin<AFMT>(&at)[MT], int wi) {
+      const int kb = wi < nwin ? 4 * (wbeg + wi) + g : (1 << 24);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) load_a<AFMT>(at[mt], ar, asr, args, arow[mt], rv[mt], kb);
+    };
+    if constexpr (AHEAD) {
+      WinBuf<AFMT, MT> buf[NBUF];
 #pragma unroll
       for (int i = 0; i < NBUF - 1; ++i) {
-        if (wbeg + i < wend) {
-          load_w(buf[i].w, pcode, pscale, wbeg + i);
-          load_a<AFMT>(buf[i].a, args, arow, rv, 4 * (wbeg + i) + g);
-        }
+        load_w(buf[i].w, wr, lane, i);
+        load_tile(buf[i].a, i);
       }
-      for (int w0 = wbeg; w0 < wend; w0 += NBUF) {
+      for (int w0 = 0; w0 < nwin; w0 += NBUF) {
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
-          const int w = w0 + u;
-          if (w < wend) {
-            const int wn = w + NBUF - 1;
-            if (wn < wend) {
-              load_w(buf[(u + NBUF - 1) % NBUF].w, pcode, pscale, wn);
-              load_a<AFMT>(buf[(u + NBUF - 1) % NBUF].a, args, arow, rv, 4 * wn + g);
-            }
-            compute_window<AFMT>(acc, buf[u].w, buf[u].a);
-          }
+          WinBuf<AFMT, MT>& nb = buf[(u + NBUF - 1) % NBUF];
+          load_w(nb.w, wr, lane, w0 + u + NBUF - 1);
+          load_tile(nb.a, w0 + u + NBUF - 1);
+          if (w0 + u < nwin) compute_window<AFMT, MT>(acc, buf[u].w, buf[u].a);
+        }
+      }
+    } else {
+      WWin wb[NBUF];
+#pragma unroll
+      for (int i = 0; i < NBUF - 1; ++i) load_w(wb[i], wr, lane, i);
+      for (int w0 = 0; w0 < nwin; w0 += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+          ATile<AFMT, MT> at;
+          load_tile(at.a, w0 + u);
+          load_w(wb[(u + NBUF - 1) % NBUF], wr, lane, w0 + u + NBUF - 1);
+          if (w0 + u < nwin) compute_window<AFMT, MT>(acc, wb[u], at.a);
         }
       }
     }
 
     if constexpr (KSPLIT > 1) {
-      if (ks > 0) {
+      // tree: at each level the upper half of the active waves hands its sums to the lower half
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) red[((ks - 1) * 4 + rt) * 64 + lane] = acc[rt];
-      }
-      __syncthreads();
-      if (ks == 0) {
+      for (int half = KSPLIT / 2; half >= 1; half >>= 1) {
+        if (ks >= half && ks < 2 * half) {
 #pragma unroll
-        for (int k2 = 1; k2 < KSPLIT; ++k2)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) acc[rt] += red[((k2 - 1) * 4 + rt) * 64 + lane];
+            for (int rt = 0; rt < 4; ++rt) red[(((ks - half) * MT + mt) * 4 + rt) * 64 + lane] = acc[mt][rt];
+        }
+        __syncthreads();
+        if (ks < half) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) acc[mt][rt] += red[((ks * MT + mt) * 4 + rt) * 64 + lane];
+        }
+        __syncthreads();
       }
     }
-    if (panel_ok && ks == 0) epilogue(args, acc, panel, mb, r1, lane);
-    if constexpr (KSPLIT > 1) __syncthreads();
+    if (panel_ok && ks == 0) {
+      for (int mt = 0; mt < MT && mb + 16 * mt < r1; ++mt) {
+        // copy tile mt out with static indices (the loop itself stays rolled)
+        f32x4 tile[4];
+#pragma unroll
+        for (int m2 = 0; m2 < MT; ++m2)
+          if (m2 == mt) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) tile[rt] = acc[m2][rt];
+          }
+        epilogue(args, tile, panel, mb + 16 * mt, r1, lane);
+      }
+    }
   }
 }
 
-template <int TAG>
-static hipError_t launch_tagged(const GemmArgs& a, int ksplit, int grid_y, hipStream_t s) {
-  constexpr int NB = 3;
-  if (ksplit == 1) {
-    dim3 grid((unsigned)ceil_div(a.P, 4), (unsigned)grid_y);
-    if (a.a_fmt == A_BF16)
-      hipLaunchKernelGGL((panel_gemm_kernel<1, A_BF16, NB, TAG>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((panel_gemm_kernel<1, A_MXFP8, NB, TAG>), grid, dim3(256), 0, s, a);
-  } else if (ksplit == 4) {
-    dim3 grid((unsigned)a.P, (unsigned)grid_y);
-    if (a.a_fmt == A_BF16)
-      hipLaunchKernelGGL((panel_gemm_kernel<4, A_BF16, NB, TAG>), grid, dim3(256), 0, s, a);
-    else
-      return hipErrorInvalidValue;
+template <int KSPLIT, int AFMT, int NBUF, int MT, bool AHEAD, int TAG>
+static void launch_one(GemmArgs a, hipStream_t s) {
+  constexpr int ppb = BlockShape<KSPLIT>::panels;
+  const int pblocks = (int)ceil_div(a.P, ppb);
+  dim3 grid;
+  if (a.offsets) {
+    grid = dim3((unsigned)pblocks, (unsigned)a.n_groups);
   } else {
-    return hipErrorInvalidValue;
+    a.m_passes = (int)ceil_div(a.M, 16 * MT);
+    grid = dim3((unsigned)(ceil_div(pblocks, 8) * 8 * a.m_passes));
   }
-  return hipGetLastError();
+  hipLaunchKernelGGL((panel_gemm_kernel<KSPLIT, AFMT, NBUF, MT, AHEAD, TAG>), grid, dim3(64 * BlockShape<KSPLIT>::waves),
+                     0, s, a);
 }
 
-hipError_t launch_panel_gemm(const GemmArgs& a, int ksplit, int grid_y, GemmStage stage, hipStream_t s) {
-  if (grid_y <= 0 || a.P <= 0) return hipSuccess;
+hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) {
+  if (a.P <= 0) return hipSuccess;
+  if (a.offsets == nullptr && a.M <= 0) return hipSuccess;
   switch (stage) {
     case GEMM_X:
-      return launch_tagged<GEMM_X>(a, ksplit, grid_y, s);
+      launch_one<8, A_BF16, 3, 1, true, GEMM_X>(a, s);
+      break;
+    case GEMM_Y:
+      launch_one<8, A_BF16, 3, 1, true, GEMM_Y>(a, s);
+      break;
     case GEMM_GATEUP:
-      return launch_tagged<GEMM_GATEUP>(a, ksplit, grid_y, s);
+      if (a.a_fmt == A_BF16)
+        launch_one<1, A_BF16, 3, 1, true, GEMM_GATEUP>(a, s);
+      else
+        launch_one<1, A_MXFP8, 3, 1, true, GEMM_GATEUP>(a, s);
+      break;
     case GEMM_DOWN:
-      return launch_tagged<GEMM_DOWN>(a, ksplit, grid_y, s);
+      if (a.a_fmt == A_BF16)
+        launch_one<1, A_BF16, 3, 1, true, GEMM_DOWN>(a, s);
+      else
+        launch_one<1, A_MXFP8, 3, 1, true, GEMM_DOWN>(a, s);
+      break;
     default:
-      return launch_tagged<GEMM_Y>(a, ksplit, grid_y, s);
+      return hipErrorInvalidValue;
   }
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------------
 // Router top-k (eq. 13): per token, the k largest keys s + b in descending order (equal keys:
 // lower expert first), and p_j = s_j / sum of the selected s. One wave per token; lane l holds
-// experts l, l + 64, ...; k rounds of lane-local best then a wave argmax.
+// experts l, l + 64, ... Each (key, expert) pair is packed into one 64-bit integer that orders
+// exactly like the rule (order-preserving key bits above, inverted expert id below), so a round
+// is one wave max; only the lane that owned the winner rescans its entries.
 // ---------------------------------------------------------------------------------------------
+typedef unsigned long long u64;
+
+__device__ __forceinline__ u64 topk_pack(float key, int e) {
+  const u32 b = __float_as_uint(key);
+  const u32 ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // monotone in key
+  return ((u64)ord << 32) | (u64)(0xFFFFFFFFu - (u32)e);
+}
+
+__device__ __forceinline__ u64 wave_max_u64(u64 v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const u32 lo = __shfl_xor((u32)v, off);
+    const u32 hi = __shfl_xor((u32)(v >> 32), off);
+    const u64 o = ((u64)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
 template <int NPER>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores, const float* __restrict__ bias,
                                                    int T, int E, int k, int32_t* __restrict__ idx,
@@ -463,53 +557,41 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform over the wave
-  float key[NPER], sv[NPER];
+  const float* srow = scores + (int64_t)t * E;
+  float sv[NPER], bv[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {  // all loads in flight together (clamped index, no branch)
+    const int e = min(lane + 64 * i, E - 1);
+    sv[i] = srow[e];
+    bv[i] = bias[e];
+  }
+  u64 key[NPER];
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + 64 * i;
-    if (e < E) {
-      sv[i] = scores[(int64_t)t * E + e];
-      const float kk = sv[i] + bias[e];
-      key[i] = kk == kk ? kk : -INFINITY;  // a NaN key ranks last, so k valid experts are always chosen
-    } else {
-      sv[i] = 0.0f;
-      key[i] = -INFINITY;
-    }
+    const float kk = sv[i] + bv[i];
+    // entries past E rank below every real entry; a NaN key ranks with -inf
+    key[i] = e < E ? topk_pack(kk == kk ? kk : -INFINITY, e) : 0ull;
   }
-  u32 taken = 0;
+  u64 best = 0ull;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) best = key[i] > best ? key[i] : best;
   int my_e = 0;
-  float my_s = 0.0f;
   for (int jj = 0; jj < k; ++jj) {
-    float bk = -INFINITY, bs = 0.0f;
-    int be = 0x7FFFFFFF;
+    const u64 w = wave_max_u64(best);
+    const int e = (int)(0xFFFFFFFFu - (u32)w);
+    if (lane == jj) my_e = e;
+    if ((e & 63) == lane) {  // the owner drops the winner and rescans
+      best = 0ull;
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-      const int e = lane + 64 * i;
-      const bool free_ = !((taken >> i) & 1u);
-      if (free_ && e < E && (key[i] > bk || (key[i] == bk && e < be))) {
-        bk = key[i];
-        be = e;
-        bs = sv[i];
+      for (int i = 0; i < NPER; ++i) {
+        if (key[i] == w) key[i] = 0ull;
+        best = key[i] > best ? key[i] : best;
       }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ok = __shfl_xor(bk, off);
-      const int oe = __shfl_xor(be, off);
-      const float os = __shfl_xor(bs, off);
-      if (ok > bk || (ok == bk && oe < be)) {
-        bk = ok;
-        be = oe;
-        bs = os;
-      }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == jj) {
-      my_e = be;
-      my_s = bs;
     }
   }
-  float sum = lane < k ? my_s : 0.0f;
+  const float my_s = lane < k ? srow[my_e] : 0.0f;
+  float sum = my_s;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
   if (lane < k) {
@@ -615,7 +697,7 @@ hipError_t launch_route(const int32_t* idx, int T, int E, int k, int32_t* counts
 // Combine + RMSNorm (eq. 11): u_t = sum_j p_tj O[inv[t, j]] in selection order, then
 // n_t = bf16(gamma * u_t / sqrt(mean(u_t^2) + eps)). One block per token.
 // ---------------------------------------------------------------------------------------------
-constexpr int kCombineThreads = 256;
+constexpr int kCombineThreads = 1024;
 constexpr int kMaxWidth = 8192;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ O,
