@@ -458,6 +458,9 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
   HIPCHECK(ctx, mark(ST_ROUTE, 0), "event");
   HIPCHECK(ctx, launch_route(idx, T, E, k, counts, offsets, perm, inv, s), "route launch");
   HIPCHECK(ctx, mark(ST_ROUTE, 1), "event");
+  // Experts averaging 32 or more rows use the LDS-tiled scaled-MFMA kernel (MXFP8 activations;
+  // its DMAs move whole 4-byte scale words, so both reduction widths must be multiples of 128)
+  const int many_rows = ((int64_t)T * k >= (int64_t)32 * E && le % 128 == 0 && h % 128 == 0) ? 1 : 0;
   // ---- gateup
   {
     GemmArgs a{};
@@ -483,6 +486,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     a.rowmap = perm;
     a.offsets = offsets;
     a.n_groups = E;
+    a.many_rows = many_rows;
     EpiSeg& sg = a.seg[0];
     sg.p0 = 0;
     sg.p1 = ctx->gu_P;
@@ -518,6 +522,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     a.as_bytes = (int64_t)T * k * (h / 32);
     a.offsets = offsets;
     a.n_groups = E;
+    a.many_rows = many_rows;
     EpiSeg& sg = a.seg[0];
     sg.p0 = 0;
     sg.p1 = ctx->dn_P;

@@ -96,6 +96,7 @@ struct GemmArgs {
   int32_t n_groups;        // grouped: number of groups
   int32_t M;               // dense: rows
   int32_t m_passes;        // dense: row passes (set by the launcher)
+  int32_t many_rows;       // grouped: rows per group large enough for the LDS-tiled scaled-MFMA kernel
   int32_t nseg;
   EpiSeg seg[kMaxSeg];
 };

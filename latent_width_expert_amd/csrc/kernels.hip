@@ -242,12 +242,20 @@ __device__ __forceinline__ void compute_window(f32x4 (&acc)[MT][4], const WWin& 
   }
 }
 
+// Maximum over each 16-lane row of the wave with DPP moves (quad swaps, then half-row and row
+// mirrors): every lane of the row ends with the row maximum.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
 // MX encode a block of 32 values held as v0 (column j) and v1 (column 16 + j) by the 16 lanes of
 // one lane group; returns the E4M3 codes of v0, v1 and the E8M0 byte. All 64 lanes must call.
 __device__ __forceinline__ void mxfp8_block(float v0, float v1, u32& c0, u32& c1, u32& sbyte) {
-  float amax = fmaxf(fabsf(v0), fabsf(v1));
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float amax = row16_max(fmaxf(fabsf(v0), fabsf(v1)));
   if (amax == 0.0f) {
     sbyte = 0;
     c0 = (__float_as_uint(v0) >> 24) & 0x80u;
@@ -481,6 +489,368 @@ __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_ker
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Grouped GEMM on scaled MFMA: MXFP8 activations x MXFP4 weights (many rows per expert).
+//
+// v_mfma_scale_f32_16x16x128_f8f6f4 takes E4M3 A and E2M1 B with their E8M0 block scales and
+// accumulates in fp32, so neither operand is converted. Operand lanes (gfx950, established on
+// the device): fp8 A lane (i = l % 16, g = l / 16) holds row i, K bytes [16 g, 16 g + 16) and
+// [64 + 16 g, 64 + 16 g + 16) of the 128-wide window; fp4 B lane (j, g) holds weight row j, K
+// [32 g, 32 g + 32) -- exactly one lane's 16 bytes of a packed panel-window; the scale operand of
+// lane (r, g) is the scale of row r, K block g (a byte of a 32-bit register chosen by opsel).
+//
+// A block of WN x WM waves covers WN panels (64 weight rows each) and a chunk of up to 64 WM
+// rows of one expert. Each panel-window is read from HBM once per chunk: the block copies it
+// into an LDS ring with LDS-DMA loads (buffer_load ... lds) DB windows ahead, and the WM waves
+// sharing a panel read their operands from LDS. Each wave gathers its own rows of A (through the
+// dispatch permutation) into a register ring DA windows ahead. One barrier per window; all
+// loads are issued unconditionally (out-of-range ones read zeros without memory traffic), so a
+// single explicit wait count covers both rings.
+// The wave's 16-row tiles are strided (tile mt of wave pm is rows 16 (mt WM + pm) ..), so a
+// partly filled chunk spreads its work evenly over the SIMDs; empty tiles skip their MFMAs.
+// ---------------------------------------------------------------------------------------------
+typedef int i32x8 __attribute__((__vector_size__(8 * sizeof(int))));
+
+struct F8Tile {
+  u32x4 lo, hi;  // K bytes [16 g, +16) and [64 + 16 g, +16) of the lane's row
+  u32 sc;        // E8M0 of (row, K block g)
+};
+
+__device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t* lds, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, kNT);
+}
+__device__ __forceinline__ void lds_dma4(rsrc_t r, uint8_t* lds, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, off, 0, 0, kNT);
+}
+
+// The four 16-byte codes and the scale word of one lane of a panel-window, read from LDS. Written
+// as one asm block (it ends with its own lgkmcnt wait) so the compiler does not order these
+// reads after every LDS DMA still in flight: the caller's vmcnt wait and barrier already
+// guarantee this stage has landed, while the DMAs of later stages keep streaming.
+__device__ __forceinline__ void lds_read_panel(const uint8_t* codes, const uint8_t* scales, u32x4 (&c)[4], u32& sc) {
+  const u32 ac = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)codes;
+  const u32 as = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)scales;
+  asm volatile(
+      "ds_read_b128 %0, %5\n\t"
+      "ds_read_b128 %1, %5 offset:1024\n\t"
+      "ds_read_b128 %2, %5 offset:2048\n\t"
+      "ds_read_b128 %3, %5 offset:3072\n\t"
+      "ds_read_b32 %4, %6\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(c[0]), "=v"(c[1]), "=v"(c[2]), "=v"(c[3]), "=v"(sc)
+      : "v"(ac), "v"(as)
+      : "memory");
+}
+
+// One fp8 A operand from an LDS stage: the two 16-byte halves and the scale byte (as above, one
+// asm block that ends with its own lgkmcnt wait).
+__device__ __forceinline__ void lds_read_atile(const uint8_t* lo_p, const uint8_t* hi_p, const uint8_t* sc_p, u32x4& lo,
+                                               u32x4& hi, u32& sc) {
+  const u32 al = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lo_p;
+  const u32 ah = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)hi_p;
+  const u32 as = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)sc_p;
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b128 %1, %4\n\t"
+      "ds_read_u8 %2, %5\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(lo), "=v"(hi), "=v"(sc)
+      : "v"(al), "v"(ah), "v"(as)
+      : "memory");
+}
+
+// Split form of the A-operand read: issue the three LDS reads now, wait later. The wait is tied
+// to the destination registers ("+v"), so their uses cannot move above it.
+__device__ __forceinline__ void lds_issue_atile(const uint8_t* lo_p, const uint8_t* hi_p, const uint8_t* sc_p,
+                                                u32x4& lo, u32x4& hi, u32& sc) {
+  const u32 al = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lo_p;
+  const u32 ah = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)hi_p;
+  const u32 as = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)sc_p;
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b128 %1, %4\n\t"
+      "ds_read_u8 %2, %5"
+      : "=&v"(lo), "=&v"(hi), "=&v"(sc)
+      : "v"(al), "v"(ah), "v"(as)
+      : "memory");
+}
+__device__ __forceinline__ void lds_wait_atile(u32x4& lo, u32x4& hi, u32& sc) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo), "+v"(hi), "+v"(sc) : : "memory");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int WN, int WM, int DA, int DB, int TAG>
+__global__ __launch_bounds__(64 * WM) void grouped_f8_kernel(GemmArgs args) {
+  // Block: WM waves (one per SIMD), tile = 64 WM rows x WN panels (64 WN columns); wave pm owns the
+  // 16-row tiles pm, pm + WM, ... (strided, so a partly filled chunk keeps the SIMDs balanced) of
+  // every panel: 4 row tiles x 4 WN column tiles of 16x16.
+  constexpr int MT = 4;
+  constexpr int ROWS = 16 * MT * WM;            // rows per chunk
+  constexpr int NA = DA + 1, NB = DB + 1;       // ring depths
+  // A stage: ROWS x 128 code bytes (16-byte chunk c of row r at position c ^ (r & 7)), then
+  // ROWS x 4 scale bytes. B stage: WN x 4096 code bytes as packed, then a 1 KB scale region.
+  constexpr int A_SC = ROWS * 128;
+  constexpr int A_STAGE = A_SC + ROWS * 4;
+  constexpr int B_SC = WN * 4096;
+  constexpr int B_STAGE = B_SC + 1024;
+  constexpr int A_DMA = ROWS / 8;               // 1 KB code DMAs per A stage (8 rows each)
+  constexpr int A_SDMA = ROWS / 64;             // 256 B scale DMAs per A stage (64 rows each)
+  constexpr int B_DMA = 4 * WN + 1;
+  static_assert(A_DMA % WM == 0 && A_SDMA % WM == 0 && 16 * WN <= 64, "tile shape");
+  constexpr int APW = A_DMA / WM, ASPW = A_SDMA / WM, BPW = (B_DMA + WM - 1) / WM;
+  constexpr int LPW = APW + ASPW + BPW;         // DMAs per wave and step
+  __shared__ __attribute__((aligned(16))) uint8_t asm_[NA][A_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t bsm[NB][B_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sink[1024];
+
+  const int lane = threadIdx.x & 63;
+  const int pm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = args.offsets ? (int)blockIdx.y : 0;
+  int r0, r1;
+  if (args.offsets) {
+    r0 = args.offsets[grp];
+    r1 = args.offsets[grp + 1];
+  } else {
+    r0 = blockIdx.y * ROWS;
+    r1 = min(r0 + ROWS, args.M);
+  }
+  const int panel0 = blockIdx.x * WN;
+  if (r0 >= r1 || panel0 >= args.P) return;  // uniform over the block
+  const int npan = min(WN, args.P - panel0);
+  const int nwin = args.wwin;
+  const rsrc_t wr = make_rsrc(args.W + (int64_t)grp * args.w_group_stride + (int64_t)panel0 * nwin * kPanelWinBytes,
+                              (int64_t)npan * nwin * kPanelWinBytes);
+  const rsrc_t ar = make_rsrc(args.A, args.a_bytes);
+  const rsrc_t asr = make_rsrc(args.A_scales, args.as_bytes);
+  const int g = lane >> 4, i16 = lane & 15;
+
+  auto issue_b = [&](int w) {
+    uint8_t* st = bsm[w % NB];
+#pragma unroll
+    for (int q = 0; q < BPW; ++q) {
+      const int id = pm * BPW + q;
+      int off = kOOB;
+      uint8_t* dst = sink;
+      if (id < 4 * WN) {
+        const int p = id >> 2, rt = id & 3;
+        dst = st + p * 4096 + rt * 1024;
+        if (p < npan && w < nwin) off = (p * nwin + w) * kPanelWinBytes + rt * 1024 + lane * 16;
+      } else if (id == 4 * WN) {
+        dst = st + B_SC;
+        const int p = lane >> 4;
+        if (p < npan && w < nwin) off = (p * nwin + w) * kPanelWinBytes + 4096 + (lane & 15) * 16;
+      }
+      lds_dma16(wr, dst, off);
+    }
+  };
+
+  for (int mb = r0; mb < r1; mb += ROWS) {
+    // this wave's A DMAs: code instructions j = pm * APW + jj cover rows 8 j .. 8 j + 7 (lane L:
+    // row 8 j + L / 8, position L % 8 holding chunk (L % 8) ^ (row & 7)); scale instructions cover
+    // 64 rows each (lane L: row 64 s + L).
+    // (the row lookups are issued together: clamped indices, no branch per load)
+    int acode[APW], ascale[ASPW];
+#pragma unroll
+    for (int jj = 0; jj < APW; ++jj) {
+      const int row = mb + 8 * (pm * APW + jj) + (lane >> 3);
+      acode[jj] = args.rowmap ? args.rowmap[min(row, r1 - 1)] : row;
+    }
+#pragma unroll
+    for (int ss = 0; ss < ASPW; ++ss) {
+      const int row = mb + 64 * (pm * ASPW + ss) + lane;
+      ascale[ss] = args.rowmap ? args.rowmap[min(row, r1 - 1)] : row;
+    }
+#pragma unroll
+    for (int jj = 0; jj < APW; ++jj) {
+      const int r = 8 * (pm * APW + jj) + (lane >> 3);
+      const int c = (lane & 7) ^ (r & 7);
+      acode[jj] = mb + r < r1 ? acode[jj] * (int)args.lda + 16 * c : -1;
+    }
+#pragma unroll
+    for (int ss = 0; ss < ASPW; ++ss)
+      ascale[ss] = mb + 64 * (pm * ASPW + ss) + lane < r1 ? ascale[ss] * (int)args.ldas : -1;
+    auto issue_a = [&](int w) {
+      uint8_t* st = asm_[w % NA];
+      const bool in = w < nwin;
+#pragma unroll
+      for (int jj = 0; jj < APW; ++jj) {
+        const int k0 = 128 * w + 16 * ((lane & 7) ^ (((8 * (pm * APW + jj)) + (lane >> 3)) & 7));
+        lds_dma16(ar, st + 1024 * (pm * APW + jj),
+                  in && acode[jj] >= 0 && k0 < args.K ? acode[jj] + 128 * w : kOOB);
+      }
+#pragma unroll
+      for (int ss = 0; ss < ASPW; ++ss)
+        lds_dma4(asr, st + A_SC + 256 * (pm * ASPW + ss), in && ascale[ss] >= 0 ? ascale[ss] + 4 * w : kOOB);
+    };
+    // 16-row tiles of this wave that hold rows (uniform)
+    bool ton[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) ton[mt] = mb + 16 * (mt * WM + pm) < r1;
+
+    f32x4 acc[MT][4 * WN];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ct = 0; ct < 4 * WN; ++ct) acc[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // prologue in steady-state order: step i issues A(i + DA), then B(i + DB)
+#pragma unroll
+    for (int i = -DB; i < 0; ++i) {
+      if (i + DA >= 0) issue_a(i + DA);
+      else {
+#pragma unroll
+        for (int q = 0; q < APW; ++q) lds_dma16(ar, sink, kOOB);
+#pragma unroll
+        for (int q = 0; q < ASPW; ++q) lds_dma4(asr, sink, kOOB);
+      }
+      issue_b(i + DB);
+    }
+    for (int w = 0; w < nwin; ++w) {
+      // A(w) was issued DA steps ago and followed by (DA - 1) full steps plus B(w + DB - DA + 1);
+      // B(w) is older still.
+      wait_vmcnt<(DA - 1) * LPW + BPW>();
+      __builtin_amdgcn_s_barrier();  // stage w complete for every wave; stages of w - 1 free
+      issue_a(w + DA);
+      issue_b(w + DB);
+      // operands of step w from LDS (asm: the compiler must not order these reads after the DMAs
+      // still in flight for later stages)
+      const uint8_t* sa = asm_[w % NA];
+      const uint8_t* sb = bsm[w % NB];
+      u32x4 bc[4 * WN];
+      u32 bs[WN];
+#pragma unroll
+      for (int p = 0; p < WN; ++p) {
+        lds_read_panel(sb + p * 4096 + lane * 16, sb + B_SC + p * 256 + lane * 4,
+                       *reinterpret_cast<u32x4(*)[4]>(&bc[4 * p]), bs[p]);
+      }
+      // row tiles in use form a prefix (tiles are strided over the waves); the operands of tile
+      // mt + 1 are read from LDS while the MFMAs of tile mt run
+      auto atile_addr = [&](int mt, const uint8_t*& lo_p, const uint8_t*& hi_p, const uint8_t*& sc_p) {
+        const int r = 16 * (mt * WM + pm) + i16;
+        lo_p = sa + r * 128 + 16 * (g ^ (r & 7));
+        hi_p = sa + r * 128 + 16 * ((4 + g) ^ (r & 7));
+        sc_p = sa + A_SC + r * 4 + g;
+      };
+      F8Tile cur, nxt;
+      if (ton[0]) {
+        const uint8_t *lp, *hp, *sp;
+        atile_addr(0, lp, hp, sp);
+        lds_issue_atile(lp, hp, sp, cur.lo, cur.hi, cur.sc);
+        lds_wait_atile(cur.lo, cur.hi, cur.sc);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (!ton[mt]) break;
+        const bool more = mt + 1 < MT && ton[mt + 1];
+        if (more) {
+          const uint8_t *lp, *hp, *sp;
+          atile_addr(mt + 1, lp, hp, sp);
+          lds_issue_atile(lp, hp, sp, nxt.lo, nxt.hi, nxt.sc);
+        }
+        const i32x8 aop = {(int)cur.lo[0], (int)cur.lo[1], (int)cur.lo[2], (int)cur.lo[3],
+                           (int)cur.hi[0], (int)cur.hi[1], (int)cur.hi[2], (int)cur.hi[3]};
+#pragma unroll
+        for (int ct = 0; ct < 4 * WN; ++ct) {
+          const i32x8 bop = {(int)bc[ct][0], (int)bc[ct][1], (int)bc[ct][2], (int)bc[ct][3], 0, 0, 0, 0};
+          acc[mt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc[mt][ct], 0, 4, 0, (int)cur.sc,
+                                                                          0, (int)(bs[ct >> 2] >> (8 * (ct & 3))));
+        }
+        if (more) {
+          lds_wait_atile(nxt.lo, nxt.hi, nxt.sc);
+          cur = nxt;
+        }
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();  // rings idle: the A ring becomes the epilogue's staging area
+    const EpiSeg& sg = args.seg[0];
+    if (sg.mode == EPI_SWIGLU_MXFP8 && sg.p0 == 0 && sg.col0 % 32 == 0 && sg.ldo % 16 == 0) {
+      // SiLU(gate) * up, MX-encoded per 32 units; codes staged per wave as [64 rows][32 WN bytes]
+      // (+ [64 rows][WN] scale bytes), then written as 16-byte row segments.
+      // lane indices re-derived here (opaque to the compiler) so that the epilogue's addresses are
+      // not hoisted out of the chunk loop and kept live through the main loop
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int g = ln >> 4, i16 = ln & 15;
+      uint8_t* stg = &asm_[0][0] + pm * (64 * 32 * WN + 64 * WN);
+      uint8_t* stg_sc = stg + 64 * 32 * WN;
+      // straight-line over every tile of the wave (tiles past the rows hold zeros; their staged
+      // codes are never written out). The optional fp32 tap goes through buffer stores whose
+      // out-of-range lanes are dropped by the hardware.
+      const bool tap = sg.pre != nullptr;
+      const rsrc_t prr = make_rsrc(sg.pre, tap ? (int64_t)r1 * sg.ldpre * 4 : 0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int p = 0; p < WN; ++p) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float v0 = silu(acc[mt][4 * p + 0][r]) * acc[mt][4 * p + 1][r];
+            const float v1 = silu(acc[mt][4 * p + 2][r]) * acc[mt][4 * p + 3][r];
+            const int lr = 16 * mt + 4 * g + r;
+            if (tap) {
+              const int row = mb + 16 * (mt * WM + pm) + 4 * g + r;
+              const int o = row * (int)sg.ldpre + sg.col0 + 32 * (panel0 + p) + i16;
+              const bool ok = row < r1 && p < npan;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), prr, ok ? 4 * o : kOOB, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), prr, ok ? 4 * (o + 16) : kOOB, 0, 0);
+            }
+            u32 c0, c1, sb;
+            mxfp8_block(v0, v1, c0, c1, sb);
+            stg[lr * 32 * WN + 32 * p + i16] = (uint8_t)c0;
+            stg[lr * 32 * WN + 32 * p + 16 + i16] = (uint8_t)c1;
+            stg_sc[lr * WN + p] = (uint8_t)sb;  // the 16 lanes of the block agree
+          }
+        }
+      }
+      __syncthreads();
+      // row segments: 2 WN 16-byte pieces per row, 64 rows
+      constexpr int PIECES = 64 * 2 * WN;
+#pragma unroll
+      for (int q = 0; q < PIECES / 64; ++q) {
+        const int id = q * 64 + ln;
+        const int lr = id / (2 * WN), piece = id % (2 * WN);
+        const int row = mb + 16 * ((lr >> 4) * WM + pm) + (lr & 15);
+        if (row < r1 && piece < 2 * npan) {
+          const u32x4 v = *(const u32x4*)(stg + lr * 32 * WN + 16 * piece);
+          *(u32x4*)((uint8_t*)sg.out + (int64_t)row * sg.ldo + sg.col0 + 32 * panel0 + 16 * piece) = v;
+        }
+      }
+      {
+        const int lr = ln;
+        const int row = mb + 16 * ((lr >> 4) * WM + pm) + (lr & 15);
+        if (row < r1) {
+          for (int p = 0; p < npan; ++p)
+            sg.out_scales[(int64_t)row * sg.ldos + (sg.col0 + 32 * panel0) / 32 + p] = stg_sc[lr * WN + p];
+        }
+      }
+    } else {
+      for (int mt = 0; mt < MT; ++mt) {
+        if (!ton[mt]) continue;
+        for (int p = 0; p < npan; ++p) {
+          f32x4 tile[4];
+#pragma unroll
+          for (int m2 = 0; m2 < MT; ++m2)
+#pragma unroll
+            for (int p2 = 0; p2 < WN; ++p2)
+              if (m2 == mt && p2 == p) {
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) tile[rt] = acc[m2][4 * p2 + rt];
+              }
+          epilogue(args, tile, panel0 + p, mb + 16 * (mt * WM + pm), r1, lane);
+        }
+      }
+    }
+    __syncthreads();  // staging and rings are reused by the next chunk
+  }
+}
+
 template <int KSPLIT, int AFMT, int NBUF, int MT, bool AHEAD, int TAG>
 static void launch_one(GemmArgs a, hipStream_t s) {
   constexpr int ppb = BlockShape<KSPLIT>::panels;
@@ -496,6 +866,13 @@ static void launch_one(GemmArgs a, hipStream_t s) {
                      0, s, a);
 }
 
+template <int TAG>
+static void launch_f8(const GemmArgs& a, hipStream_t s) {
+  constexpr int WN = 4, WM = 4, DA = 2, DB = 2;
+  dim3 grid((unsigned)ceil_div(a.P, WN), a.offsets ? (unsigned)a.n_groups : (unsigned)ceil_div(a.M, 64 * WM));
+  hipLaunchKernelGGL((grouped_f8_kernel<WN, WM, DA, DB, TAG>), grid, dim3(64 * WM), 0, s, a);
+}
+
 hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) {
   if (a.P <= 0) return hipSuccess;
   if (a.offsets == nullptr && a.M <= 0) return hipSuccess;
@@ -509,12 +886,16 @@ hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) 
     case GEMM_GATEUP:
       if (a.a_fmt == A_BF16)
         launch_one<1, A_BF16, 3, 1, true, GEMM_GATEUP>(a, s);
+      else if (a.many_rows)
+        launch_f8<GEMM_GATEUP>(a, s);
       else
         launch_one<1, A_MXFP8, 3, 1, true, GEMM_GATEUP>(a, s);
       break;
     case GEMM_DOWN:
       if (a.a_fmt == A_BF16)
         launch_one<1, A_BF16, 3, 1, true, GEMM_DOWN>(a, s);
+      else if (a.many_rows)
+        launch_f8<GEMM_DOWN>(a, s);
       else
         launch_one<1, A_MXFP8, 3, 1, true, GEMM_DOWN>(a, s);
       break;

@@ -158,7 +158,8 @@ class Result:
     taps: dict = field(default_factory=dict)
 
 
-def forward(x_bits, weights, shape, select_override=None, keep_expert_rows=True) -> Result:
+def forward(x_bits, weights, shape, select_override=None, keep_expert_rows=True, z_override=None,
+            h_override=None) -> Result:
     """The layer on a batch of tokens.
 
     x_bits: bf16 bit patterns [T, d]. weights: object with w_router(), w_down(), w_up(),
@@ -167,6 +168,11 @@ def forward(x_bits, weights, shape, select_override=None, keep_expert_rows=True)
     select_override: optional {token index: sequence of k expert ids} used instead of
     the oracle's own top-k for those tokens (to score a GPU selection that differs
     only inside the tie tolerance).
+    z_override [T, l] / h_override [T, k, h]: optional values after the quantisation point
+    of the latent z / the GLU hidden of (token, selection slot), used instead of the
+    oracle's own quantisation, so that a quantisation decision is taken on the value the
+    compared implementation computed (its codes are checked against this oracle's encoder
+    separately).
     """
     s_ = shape
     xh = mx.bf16_from_bits(x_bits)
@@ -188,6 +194,8 @@ def forward(x_bits, weights, shape, select_override=None, keep_expert_rows=True)
     if s_.latent_moe:
         z = xh @ dequant(weights.w_down()).T
         zq, zc, zs = q_act(z, s_.act)
+        if z_override is not None:
+            zq = np.asarray(z_override, np.float64)
         taps.update(z=z, zq=zq, z_codes=zc, z_scales=zs)
     else:
         zq = xh
@@ -200,11 +208,16 @@ def forward(x_bits, weights, shape, select_override=None, keep_expert_rows=True)
     rows_out = np.zeros((T * s_.k, width))
     rows_h = np.zeros((T * s_.k, s_.h)) if keep_expert_rows else None
     rows_hpre = np.zeros((T * s_.k, s_.h)) if keep_expert_rows else None
+    row_tj = np.empty((T * s_.k, 2), np.int64)          # dispatched row -> (token, slot)
+    row_tj[inv.reshape(-1)] = np.stack(np.meshgrid(np.arange(T), np.arange(s_.k), indexing="ij"), -1).reshape(-1, 2)
     for e in np.nonzero(counts)[0]:
         r0, r1 = offsets[e], offsets[e + 1]
         (gc, uc, dc) = weights.routed(int(e))
         G, U, D = dequant(_first(gc)), dequant(_first(uc)), dequant(_first(dc))
         o, hq, hpre, _, _ = glu(zq[perm[r0:r1]], G, U, D, s_.act)
+        if h_override is not None:
+            hq = np.asarray(h_override, np.float64)[row_tj[r0:r1, 0], row_tj[r0:r1, 1]]
+            o = hq @ D.T
         rows_out[r0:r1] = o
         if keep_expert_rows:
             rows_h[r0:r1] = hq

@@ -88,3 +88,62 @@ def check_routing(gpu, sel, E):
     assert np.array_equal(gpu["perm"], perm)
     assert np.array_equal(gpu["inv"].reshape(inv.shape), inv)
     return int(flip.sum())
+
+
+def decode_act(codes_or_bits, scales, act):
+    """GPU activation at its quantisation point -> fp64 values (bf16 bits, or E4M3 codes + scales)."""
+    if act == "mxfp8":
+        return mx.mx_dequantize(codes_or_bits, scales, "e4m3")
+    return mx.bf16_from_bits(codes_or_bits)
+
+
+def stagewise(g, weights, shape, x_bits):
+    """Each routed-path kernel against the oracle's definition of its step applied to the GPU's own
+    inputs (the quantisation decisions taken in the GPU's precision, pinned separately by the strict
+    encoder checks). Returns a dict of relative errors; asserts them."""
+    s = shape
+    T = x_bits.shape[0]
+    act = s.act
+    out = {}
+    if s.latent_moe:
+        zq = decode_act(g["z"], g.get("z_scales"), act)
+    else:
+        zq = mx.bf16_from_bits(x_bits)
+    hq = decode_act(g["h"], g.get("h_scales"), act)
+    perm, offsets = g["perm"], g["offsets"]
+    h_ref = np.zeros_like(g["h_f32"], dtype=np.float64)
+    o_ref = np.zeros_like(g["expert_out"], dtype=np.float64)
+    for e in np.nonzero(g["counts"])[0]:
+        r0, r1 = offsets[e], offsets[e + 1]
+        G, U, D = (layer.dequant(m) for m in _first3(weights.routed(int(e))))
+        zr = zq[perm[r0:r1]]
+        h_ref[r0:r1] = layer.silu(zr @ G.T) * (zr @ U.T)
+        o_ref[r0:r1] = hq[r0:r1] @ D.T
+    out["h"] = rel_l2(g["h_f32"], h_ref)
+    out["o"] = rel_l2(g["expert_out"], o_ref)
+    inv = g["inv"].reshape(T, s.k)
+    u_ref = np.einsum("tk,tkc->tc", g["topk_p"].astype(np.float64), g["expert_out"].astype(np.float64)[inv])
+    out["u"] = rel_l2(g["u"], u_ref)
+    # 1e-4: the fp8 x fp4 scaled MFMA accumulates with ~2^-16 relative error (measured); logic
+    # errors (a wrong row, scale or operand) show up as O(1)
+    assert out["h"] < 1e-4 and out["o"] < 1e-4 and out["u"] < 1e-6, out
+    if s.latent_moe:
+        npre = layer.rmsnorm(g["u"].astype(np.float64), weights.rms_gamma(), s.eps)
+        out["n_diff"] = int((mx.bf16_from_bits(g["n"]) != mx.bf16_round(npre)).sum())
+        assert out["n_diff"] <= max(2, 1e-3 * npre.size)
+        parity_n = rel_l2(mx.bf16_from_bits(g["n"]), npre)
+        assert parity_n < 4e-3
+    return out
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def _first3(m):
+    def one(p):
+        c, sc = p
+        return (c[0], sc[0]) if c.ndim == 3 else (c, sc)
+    return tuple(one(p) for p in m)

@@ -197,6 +197,9 @@ WORKLOADS = {
                      note="tiny LatentMoE layer, CPU seconds"),
     "tiny_mxfp8": Workload("tiny_mxfp8", LayerShape(d=256, l=128, h=96, E=16, k=4, Ns=1, hs=96, act="mxfp8"),
                            T=64, seed=0, note="tiny layer, MXFP8 latent and hidden activations"),
+    "tiny_mxfp8_many": Workload("tiny_mxfp8_many", LayerShape(d=256, l=128, h=128, E=16, k=4, Ns=1, hs=96,
+                                                              act="mxfp8"), T=512, seed=0,
+                                note="tiny layer, MXFP8, 128 rows per expert (scaled-MFMA grouped kernel)"),
     "tiny_fullwidth": Workload("tiny_fullwidth", LayerShape(d=256, l=256, h=96, E=16, k=2, Ns=1, hs=96,
                                                             latent_moe=0), T=64, seed=5,
                                note="tiny conventional full-width MoE"),
