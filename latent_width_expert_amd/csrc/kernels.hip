@@ -7,6 +7,8 @@
 
 #include <math.h>
 
+#include <utility>
+
 namespace k3 {
 
 typedef uint32_t u32;
@@ -499,15 +501,10 @@ __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_ker
 // [32 g, 32 g + 32) -- exactly one lane's 16 bytes of a packed panel-window; the scale operand of
 // lane (r, g) is the scale of row r, K block g (a byte of a 32-bit register chosen by opsel).
 //
-// A block of WN x WM waves covers WN panels (64 weight rows each) and a chunk of up to 64 WM
-// rows of one expert. Each panel-window is read from HBM once per chunk: the block copies it
-// into an LDS ring with LDS-DMA loads (buffer_load ... lds) DB windows ahead, and the WM waves
-// sharing a panel read their operands from LDS. Each wave gathers its own rows of A (through the
-// dispatch permutation) into a register ring DA windows ahead. One barrier per window; all
-// loads are issued unconditionally (out-of-range ones read zeros without memory traffic), so a
-// single explicit wait count covers both rings.
-// The wave's 16-row tiles are strided (tile mt of wave pm is rows 16 (mt WM + pm) ..), so a
-// partly filled chunk spreads its work evenly over the SIMDs; empty tiles skip their MFMAs.
+// The weights (one read of each panel-window per row chunk) stream straight into registers,
+// the activation rows shared by the block's waves go through LDS (LDS-DMA, buffer_load ... lds).
+// All loads are issued unconditionally (out-of-range ones read zeros without memory traffic), so
+// one explicit wait count per window covers both streams.
 // ---------------------------------------------------------------------------------------------
 typedef int i32x8 __attribute__((__vector_size__(8 * sizeof(int))));
 
@@ -516,66 +513,34 @@ struct F8Tile {
   u32 sc;        // E8M0 of (row, K block g)
 };
 
+// LDS-DMA of 16 / 4 bytes per lane (lane l's data lands at lds + 16 l / 4 l); default cache policy,
+// so the activation rows stay in L2 for the other panel blocks of the group.
 __device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t* lds, int off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, kNT);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
 }
 __device__ __forceinline__ void lds_dma4(rsrc_t r, uint8_t* lds, int off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, off, 0, 0, kNT);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, off, 0, 0, 0);
 }
 
-// The four 16-byte codes and the scale word of one lane of a panel-window, read from LDS. Written
-// as one asm block (it ends with its own lgkmcnt wait) so the compiler does not order these
-// reads after every LDS DMA still in flight: the caller's vmcnt wait and barrier already
-// guarantee this stage has landed, while the DMAs of later stages keep streaming.
-__device__ __forceinline__ void lds_read_panel(const uint8_t* codes, const uint8_t* scales, u32x4 (&c)[4], u32& sc) {
-  const u32 ac = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)codes;
-  const u32 as = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)scales;
+// An fp8 A operand from an LDS stage: the two 16-byte halves and the scale byte, with the tile's
+// offsets inside the stage as instruction immediates (one base register per operand part serves
+// every row tile). Written as asm so that the compiler does not order these reads after every LDS
+// DMA still in flight (the caller's vmcnt wait and barrier already guarantee the stage has
+// landed, while the DMAs of later stages keep streaming). The reads and their lgkmcnt wait are
+// one asm statement: were they split, the compiler could copy the destination registers (to
+// form the 8-register MFMA operand) between the issue and the wait, before the data arrives.
+// The MFMAs already issued keep the matrix core busy while the wave waits here.
+template <int LO, int HI, int SC>
+__device__ __forceinline__ void lds_read_atile_at(u32 lo_a, u32 hi_a, u32 sc_a, u32x4& lo, u32x4& hi, u32& sc) {
+  static_assert(LO < 65536 && HI < 65536 && SC < 65536, "ds offset range");
   asm volatile(
-      "ds_read_b128 %0, %5\n\t"
-      "ds_read_b128 %1, %5 offset:1024\n\t"
-      "ds_read_b128 %2, %5 offset:2048\n\t"
-      "ds_read_b128 %3, %5 offset:3072\n\t"
-      "ds_read_b32 %4, %6\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=v"(c[0]), "=v"(c[1]), "=v"(c[2]), "=v"(c[3]), "=v"(sc)
-      : "v"(ac), "v"(as)
-      : "memory");
-}
-
-// One fp8 A operand from an LDS stage: the two 16-byte halves and the scale byte (as above, one
-// asm block that ends with its own lgkmcnt wait).
-__device__ __forceinline__ void lds_read_atile(const uint8_t* lo_p, const uint8_t* hi_p, const uint8_t* sc_p, u32x4& lo,
-                                               u32x4& hi, u32& sc) {
-  const u32 al = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lo_p;
-  const u32 ah = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)hi_p;
-  const u32 as = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)sc_p;
-  asm volatile(
-      "ds_read_b128 %0, %3\n\t"
-      "ds_read_b128 %1, %4\n\t"
-      "ds_read_u8 %2, %5\n\t"
+      "ds_read_b128 %0, %3 offset:%6\n\t"
+      "ds_read_b128 %1, %4 offset:%7\n\t"
+      "ds_read_u8 %2, %5 offset:%8\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=v"(lo), "=v"(hi), "=v"(sc)
-      : "v"(al), "v"(ah), "v"(as)
+      : "v"(lo_a), "v"(hi_a), "v"(sc_a), "i"(LO), "i"(HI), "i"(SC)
       : "memory");
-}
-
-// Split form of the A-operand read: issue the three LDS reads now, wait later. The wait is tied
-// to the destination registers ("+v"), so their uses cannot move above it.
-__device__ __forceinline__ void lds_issue_atile(const uint8_t* lo_p, const uint8_t* hi_p, const uint8_t* sc_p,
-                                                u32x4& lo, u32x4& hi, u32& sc) {
-  const u32 al = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lo_p;
-  const u32 ah = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)hi_p;
-  const u32 as = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)sc_p;
-  asm volatile(
-      "ds_read_b128 %0, %3\n\t"
-      "ds_read_b128 %1, %4\n\t"
-      "ds_read_u8 %2, %5"
-      : "=&v"(lo), "=&v"(hi), "=&v"(sc)
-      : "v"(al), "v"(ah), "v"(as)
-      : "memory");
-}
-__device__ __forceinline__ void lds_wait_atile(u32x4& lo, u32x4& hi, u32& sc) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo), "+v"(hi), "+v"(sc) : : "memory");
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -585,86 +550,60 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int WN, int WM, int DA, int DB, int TAG>
-__global__ __launch_bounds__(64 * WM) void grouped_f8_kernel(GemmArgs args) {
-  // Block: WM waves (one per SIMD), tile = 64 WM rows x WN panels (64 WN columns); wave pm owns the
-  // 16-row tiles pm, pm + WM, ... (strided, so a partly filled chunk keeps the SIMDs balanced) of
-  // every panel: 4 row tiles x 4 WN column tiles of 16x16.
-  constexpr int MT = 4;
-  constexpr int ROWS = 16 * MT * WM;            // rows per chunk
-  constexpr int NA = DA + 1, NB = DB + 1;       // ring depths
-  // A stage: ROWS x 128 code bytes (16-byte chunk c of row r at position c ^ (r & 7)), then
-  // ROWS x 4 scale bytes. B stage: WN x 4096 code bytes as packed, then a 1 KB scale region.
+// Grouped MXFP8 x MXFP4 GEMM on the scaled MFMA, for groups with many rows (prefill).
+// Block: 4 waves on one group (expert) and 4 consecutive panels; wave pm owns panel panel0 + pm for
+// a chunk of up to 256 of the group's rows (16 row tiles x 4 column tiles of 16x16, fp32
+// accumulators). Per K window of 128:
+//   - the chunk's activation rows (E4M3 codes, E8M0 scales) are DMA'd into an LDS stage shared by
+//     the four waves, D windows ahead (16-byte chunk c of row r stored at position c ^ (r & 7));
+//   - each wave streams its own panel-window of weights into registers, D windows ahead;
+//   - one v_mfma_scale_f32_16x16x128_f8f6f4 per (row tile with rows, column tile).
+// Blocks are dealt to the XCDs so that every panel block of a group runs on the XCD of that group
+// (group g on XCD g mod 8): the group's activation rows are fetched into one L2 and re-read there.
+// EPI 0: fp32 out. EPI 1: GLU panels, SiLU(gate) * up MX-encoded (E4M3, E8M0 per 32 units),
+// staged in LDS and written as 16-byte row segments.
+template <int D, int EPI, int TAG>
+__global__ __launch_bounds__(256) void grouped_f8_kernel(GemmArgs args) {
+  constexpr int MT = 16, ROWS = 256, NA = D + 1, NBR = D + 1;
   constexpr int A_SC = ROWS * 128;
   constexpr int A_STAGE = A_SC + ROWS * 4;
-  constexpr int B_SC = WN * 4096;
-  constexpr int B_STAGE = B_SC + 1024;
-  constexpr int A_DMA = ROWS / 8;               // 1 KB code DMAs per A stage (8 rows each)
-  constexpr int A_SDMA = ROWS / 64;             // 256 B scale DMAs per A stage (64 rows each)
-  constexpr int B_DMA = 4 * WN + 1;
-  static_assert(A_DMA % WM == 0 && A_SDMA % WM == 0 && 16 * WN <= 64, "tile shape");
-  constexpr int APW = A_DMA / WM, ASPW = A_SDMA / WM, BPW = (B_DMA + WM - 1) / WM;
-  constexpr int LPW = APW + ASPW + BPW;         // DMAs per wave and step
+  constexpr int APW = ROWS / 8 / 4;  // 1 KB code DMAs per wave and window (8 rows each)
+  constexpr int LPW = APW + 1 + 5;   // + one scale DMA (64 rows) + five weight loads
+  static_assert((D - 1) * LPW < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) uint8_t asm_[NA][A_STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t bsm[NB][B_STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t sink[1024];
 
   const int lane = threadIdx.x & 63;
   const int pm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = args.offsets ? (int)blockIdx.y : 0;
-  int r0, r1;
-  if (args.offsets) {
-    r0 = args.offsets[grp];
-    r1 = args.offsets[grp + 1];
-  } else {
-    r0 = blockIdx.y * ROWS;
-    r1 = min(r0 + ROWS, args.M);
-  }
-  const int panel0 = blockIdx.x * WN;
-  if (r0 >= r1 || panel0 >= args.P) return;  // uniform over the block
-  const int npan = min(WN, args.P - panel0);
+  const int nblk = (args.P + 3) / 4;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int grp = xcd + 8 * (slot / nblk);
+  if (grp >= args.n_groups) return;
+  const int panel0 = 4 * (slot % nblk);
+  const int r0 = args.offsets[grp], r1 = args.offsets[grp + 1];
+  if (r0 >= r1) return;  // uniform over the block
+  const int npan = min(4, args.P - panel0);
+  const bool pok = pm < npan;
   const int nwin = args.wwin;
-  const rsrc_t wr = make_rsrc(args.W + (int64_t)grp * args.w_group_stride + (int64_t)panel0 * nwin * kPanelWinBytes,
-                              (int64_t)npan * nwin * kPanelWinBytes);
+  const rsrc_t wr = make_rsrc(args.W + (int64_t)grp * args.w_group_stride +
+                                  (int64_t)(pok ? panel0 + pm : 0) * nwin * kPanelWinBytes,
+                              pok ? (int64_t)nwin * kPanelWinBytes : 0);
   const rsrc_t ar = make_rsrc(args.A, args.a_bytes);
   const rsrc_t asr = make_rsrc(args.A_scales, args.as_bytes);
   const int g = lane >> 4, i16 = lane & 15;
 
-  auto issue_b = [&](int w) {
-    uint8_t* st = bsm[w % NB];
-#pragma unroll
-    for (int q = 0; q < BPW; ++q) {
-      const int id = pm * BPW + q;
-      int off = kOOB;
-      uint8_t* dst = sink;
-      if (id < 4 * WN) {
-        const int p = id >> 2, rt = id & 3;
-        dst = st + p * 4096 + rt * 1024;
-        if (p < npan && w < nwin) off = (p * nwin + w) * kPanelWinBytes + rt * 1024 + lane * 16;
-      } else if (id == 4 * WN) {
-        dst = st + B_SC;
-        const int p = lane >> 4;
-        if (p < npan && w < nwin) off = (p * nwin + w) * kPanelWinBytes + 4096 + (lane & 15) * 16;
-      }
-      lds_dma16(wr, dst, off);
-    }
-  };
-
   for (int mb = r0; mb < r1; mb += ROWS) {
-    // this wave's A DMAs: code instructions j = pm * APW + jj cover rows 8 j .. 8 j + 7 (lane L:
-    // row 8 j + L / 8, position L % 8 holding chunk (L % 8) ^ (row & 7)); scale instructions cover
-    // 64 rows each (lane L: row 64 s + L).
-    // (the row lookups are issued together: clamped indices, no branch per load)
-    int acode[APW], ascale[ASPW];
+    // A DMAs of this wave: code instruction j = pm APW + jj covers chunk rows 8 j .. 8 j + 7
+    // (lane L: row 8 j + L / 8, position L % 8 holding chunk (L % 8) ^ (row & 7)); the scale
+    // instruction covers rows 64 pm .. 64 pm + 63 (lane L: row 64 pm + L).
+    int acode[APW], ascale;
 #pragma unroll
     for (int jj = 0; jj < APW; ++jj) {
       const int row = mb + 8 * (pm * APW + jj) + (lane >> 3);
       acode[jj] = args.rowmap ? args.rowmap[min(row, r1 - 1)] : row;
     }
-#pragma unroll
-    for (int ss = 0; ss < ASPW; ++ss) {
-      const int row = mb + 64 * (pm * ASPW + ss) + lane;
-      ascale[ss] = args.rowmap ? args.rowmap[min(row, r1 - 1)] : row;
+    {
+      const int row = mb + 64 * pm + lane;
+      ascale = args.rowmap ? args.rowmap[min(row, r1 - 1)] : row;
     }
 #pragma unroll
     for (int jj = 0; jj < APW; ++jj) {
@@ -672,178 +611,151 @@ __global__ __launch_bounds__(64 * WM) void grouped_f8_kernel(GemmArgs args) {
       const int c = (lane & 7) ^ (r & 7);
       acode[jj] = mb + r < r1 ? acode[jj] * (int)args.lda + 16 * c : -1;
     }
-#pragma unroll
-    for (int ss = 0; ss < ASPW; ++ss)
-      ascale[ss] = mb + 64 * (pm * ASPW + ss) + lane < r1 ? ascale[ss] * (int)args.ldas : -1;
+    ascale = mb + 64 * pm + lane < r1 ? ascale * (int)args.ldas : -1;
     auto issue_a = [&](int w) {
       uint8_t* st = asm_[w % NA];
       const bool in = w < nwin;
 #pragma unroll
-      for (int jj = 0; jj < APW; ++jj) {
-        const int k0 = 128 * w + 16 * ((lane & 7) ^ (((8 * (pm * APW + jj)) + (lane >> 3)) & 7));
-        lds_dma16(ar, st + 1024 * (pm * APW + jj),
-                  in && acode[jj] >= 0 && k0 < args.K ? acode[jj] + 128 * w : kOOB);
-      }
-#pragma unroll
-      for (int ss = 0; ss < ASPW; ++ss)
-        lds_dma4(asr, st + A_SC + 256 * (pm * ASPW + ss), in && ascale[ss] >= 0 ? ascale[ss] + 4 * w : kOOB);
+      for (int jj = 0; jj < APW; ++jj)
+        lds_dma16(ar, st + 1024 * (pm * APW + jj), in && acode[jj] >= 0 ? acode[jj] + 128 * w : kOOB);
+      lds_dma4(asr, st + A_SC + 256 * pm, in && ascale >= 0 ? ascale + 4 * w : kOOB);
     };
-    // 16-row tiles of this wave that hold rows (uniform)
-    bool ton[MT];
+    u32x4 bw[NBR][4];
+    u32 bs[NBR];
+    auto issue_b = [&](int w, u32x4(&c)[4], u32& sc) {
+      const int off = w < nwin ? w * kPanelWinBytes : kOOB;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) ton[mt] = mb + 16 * (mt * WM + pm) < r1;
+      for (int rt = 0; rt < 4; ++rt)
+        c[rt] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + rt * 1024 + lane * 16, 0, kNT);
+      sc = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 4096 + lane * 4, 0, kNT);
+    };
+    // row tiles holding rows (uniform)
+    const int nt = min(MT, (r1 - mb + 15) / 16);
 
-    f32x4 acc[MT][4 * WN];
+    f32x4 acc[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int ct = 0; ct < 4 * WN; ++ct) acc[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // prologue in steady-state order: step i issues A(i + DA), then B(i + DB)
 #pragma unroll
-    for (int i = -DB; i < 0; ++i) {
-      if (i + DA >= 0) issue_a(i + DA);
-      else {
-#pragma unroll
-        for (int q = 0; q < APW; ++q) lds_dma16(ar, sink, kOOB);
-#pragma unroll
-        for (int q = 0; q < ASPW; ++q) lds_dma4(asr, sink, kOOB);
-      }
-      issue_b(i + DB);
+    for (int i = 0; i < D; ++i) {
+      issue_a(i);
+      issue_b(i, bw[i], bs[i]);
     }
-    for (int w = 0; w < nwin; ++w) {
-      // A(w) was issued DA steps ago and followed by (DA - 1) full steps plus B(w + DB - DA + 1);
-      // B(w) is older still.
-      wait_vmcnt<(DA - 1) * LPW + BPW>();
-      __builtin_amdgcn_s_barrier();  // stage w complete for every wave; stages of w - 1 free
-      issue_a(w + DA);
-      issue_b(w + DB);
-      // operands of step w from LDS (asm: the compiler must not order these reads after the DMAs
-      // still in flight for later stages)
-      const uint8_t* sa = asm_[w % NA];
-      const uint8_t* sb = bsm[w % NB];
-      u32x4 bc[4 * WN];
-      u32 bs[WN];
+    for (int w0 = 0; w0 < nwin; w0 += NBR) {
 #pragma unroll
-      for (int p = 0; p < WN; ++p) {
-        lds_read_panel(sb + p * 4096 + lane * 16, sb + B_SC + p * 256 + lane * 4,
-                       *reinterpret_cast<u32x4(*)[4]>(&bc[4 * p]), bs[p]);
-      }
-      // row tiles in use form a prefix (tiles are strided over the waves); the operands of tile
-      // mt + 1 are read from LDS while the MFMAs of tile mt run
-      auto atile_addr = [&](int mt, const uint8_t*& lo_p, const uint8_t*& hi_p, const uint8_t*& sc_p) {
-        const int r = 16 * (mt * WM + pm) + i16;
-        lo_p = sa + r * 128 + 16 * (g ^ (r & 7));
-        hi_p = sa + r * 128 + 16 * ((4 + g) ^ (r & 7));
-        sc_p = sa + A_SC + r * 4 + g;
-      };
-      F8Tile cur, nxt;
-      if (ton[0]) {
-        const uint8_t *lp, *hp, *sp;
-        atile_addr(0, lp, hp, sp);
-        lds_issue_atile(lp, hp, sp, cur.lo, cur.hi, cur.sc);
-        lds_wait_atile(cur.lo, cur.hi, cur.sc);
-      }
+      for (int u = 0; u < NBR; ++u) {
+        const int w = w0 + u;
+        if (w >= nwin) break;  // uniform
+        // A(w) and B(w) were issued D steps ago, followed by D - 1 steps' worth of loads
+        wait_vmcnt<(D - 1) * LPW>();
+        __builtin_amdgcn_s_barrier();  // stage w complete for every wave; stage w - 1 free
+        issue_a(w + D);
+        issue_b(w + D, bw[(u + D) % NBR], bs[(u + D) % NBR]);
+        // A operands: row tile mt of the stage sits at mt * 2048 (codes) and A_SC + mt * 64 (scales);
+        // the swizzle depends on the row only through row % 8 = i16 % 8.
+        const u32 sbase = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)asm_[w % NA];
+        const u32 lo_a = sbase + i16 * 128 + 16 * (g ^ (i16 & 7));
+        const u32 hi_a = sbase + i16 * 128 + 16 * ((4 + g) ^ (i16 & 7));
+        const u32 sc_a = sbase + i16 * 4 + g;
+        F8Tile cur;
+        lds_read_atile_at<0, 0, A_SC>(lo_a, hi_a, sc_a, cur.lo, cur.hi, cur.sc);
+        // one body per row tile (compile-time mt: immediates, static accumulator indices); tiles
+        // past the chunk's rows are skipped (uniform). The next tile's operands are read while
+        // this tile's four MFMAs run.
+        [&]<int... MTI>(std::integer_sequence<int, MTI...>) {
+          ([&] {
+            constexpr int mt = MTI;
+            if (mt < nt) {
+              const i32x8 aop = {(int)cur.lo[0], (int)cur.lo[1], (int)cur.lo[2], (int)cur.lo[3],
+                                 (int)cur.hi[0], (int)cur.hi[1], (int)cur.hi[2], (int)cur.hi[3]};
+              const int asc = (int)cur.sc;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (!ton[mt]) break;
-        const bool more = mt + 1 < MT && ton[mt + 1];
-        if (more) {
-          const uint8_t *lp, *hp, *sp;
-          atile_addr(mt + 1, lp, hp, sp);
-          lds_issue_atile(lp, hp, sp, nxt.lo, nxt.hi, nxt.sc);
-        }
-        const i32x8 aop = {(int)cur.lo[0], (int)cur.lo[1], (int)cur.lo[2], (int)cur.lo[3],
-                           (int)cur.hi[0], (int)cur.hi[1], (int)cur.hi[2], (int)cur.hi[3]};
-#pragma unroll
-        for (int ct = 0; ct < 4 * WN; ++ct) {
-          const i32x8 bop = {(int)bc[ct][0], (int)bc[ct][1], (int)bc[ct][2], (int)bc[ct][3], 0, 0, 0, 0};
-          acc[mt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc[mt][ct], 0, 4, 0, (int)cur.sc,
-                                                                          0, (int)(bs[ct >> 2] >> (8 * (ct & 3))));
-        }
-        if (more) {
-          lds_wait_atile(nxt.lo, nxt.hi, nxt.sc);
-          cur = nxt;
-        }
+              for (int ct = 0; ct < 4; ++ct) {
+                const i32x8 bop = {(int)bw[u][ct][0], (int)bw[u][ct][1], (int)bw[u][ct][2], (int)bw[u][ct][3],
+                                   0, 0, 0, 0};
+                acc[mt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc[mt][ct], 0, 4, 0, asc, 0,
+                                                                                (int)(bs[u] >> (8 * ct)));
+              }
+              if constexpr (mt + 1 < MT) {
+                if (mt + 1 < nt)
+                  lds_read_atile_at<(mt + 1) * 2048, (mt + 1) * 2048, A_SC + (mt + 1) * 64>(lo_a, hi_a, sc_a, cur.lo,
+                                                                                           cur.hi, cur.sc);
+              }
+            }
+          }(), ...);
+        }(std::make_integer_sequence<int, MT>{});
       }
     }
     wait_vmcnt<0>();
-    __syncthreads();  // rings idle: the A ring becomes the epilogue's staging area
+    __syncthreads();  // rings idle
+
+    // epilogue; lane indices re-derived (opaque to the compiler) so that no address arithmetic is
+    // hoisted out of the chunk loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int eg = ln >> 4, ej = ln & 15;
     const EpiSeg& sg = args.seg[0];
-    if (sg.mode == EPI_SWIGLU_MXFP8 && sg.p0 == 0 && sg.col0 % 32 == 0 && sg.ldo % 16 == 0) {
-      // SiLU(gate) * up, MX-encoded per 32 units; codes staged per wave as [64 rows][32 WN bytes]
-      // (+ [64 rows][WN] scale bytes), then written as 16-byte row segments.
-      // lane indices re-derived here (opaque to the compiler) so that the epilogue's addresses are
-      // not hoisted out of the chunk loop and kept live through the main loop
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int g = ln >> 4, i16 = ln & 15;
-      uint8_t* stg = &asm_[0][0] + pm * (64 * 32 * WN + 64 * WN);
-      uint8_t* stg_sc = stg + 64 * 32 * WN;
-      // straight-line over every tile of the wave (tiles past the rows hold zeros; their staged
-      // codes are never written out). The optional fp32 tap goes through buffer stores whose
-      // out-of-range lanes are dropped by the hardware.
+    const int nrow = min(ROWS, r1 - mb);
+    if constexpr (EPI == 1) {
+      // codes staged as [256 rows][128 bytes] (32 units per panel), scales as [256 rows][4]
+      uint8_t* stg = &asm_[0][0];
+      uint8_t* stg_sc = stg + ROWS * 128;
       const bool tap = sg.pre != nullptr;
-      const rsrc_t prr = make_rsrc(sg.pre, tap ? (int64_t)r1 * sg.ldpre * 4 : 0);
+      const rsrc_t prr = make_rsrc(tap ? sg.pre + (int64_t)mb * sg.ldpre : nullptr,
+                                   tap ? (int64_t)nrow * sg.ldpre * 4 : 0);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int p = 0; p < WN; ++p) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float v0 = silu(acc[mt][4 * p + 0][r]) * acc[mt][4 * p + 1][r];
-            const float v1 = silu(acc[mt][4 * p + 2][r]) * acc[mt][4 * p + 3][r];
-            const int lr = 16 * mt + 4 * g + r;
-            if (tap) {
-              const int row = mb + 16 * (mt * WM + pm) + 4 * g + r;
-              const int o = row * (int)sg.ldpre + sg.col0 + 32 * (panel0 + p) + i16;
-              const bool ok = row < r1 && p < npan;
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), prr, ok ? 4 * o : kOOB, 0, 0);
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), prr, ok ? 4 * (o + 16) : kOOB, 0, 0);
-            }
-            u32 c0, c1, sb;
-            mxfp8_block(v0, v1, c0, c1, sb);
-            stg[lr * 32 * WN + 32 * p + i16] = (uint8_t)c0;
-            stg[lr * 32 * WN + 32 * p + 16 + i16] = (uint8_t)c1;
-            stg_sc[lr * WN + p] = (uint8_t)sb;  // the 16 lanes of the block agree
+        for (int r = 0; r < 4; ++r) {
+          const float v0 = silu(acc[mt][0][r]) * acc[mt][1][r];
+          const float v1 = silu(acc[mt][2][r]) * acc[mt][3][r];
+          const int lr = 16 * mt + 4 * eg + r;
+          if (tap) {
+            const int o = lr * (int)sg.ldpre + sg.col0 + 32 * (panel0 + pm) + ej;
+            const bool ok = lr < nrow && pok;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), prr, ok ? 4 * o : kOOB, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), prr, ok ? 4 * (o + 16) : kOOB, 0, 0);
           }
+          u32 c0, c1, sb;
+          mxfp8_block(v0, v1, c0, c1, sb);
+          stg[lr * 128 + 32 * pm + ej] = (uint8_t)c0;
+          stg[lr * 128 + 32 * pm + 16 + ej] = (uint8_t)c1;
+          stg_sc[lr * 4 + pm] = (uint8_t)sb;  // the 16 lanes of the block agree
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       __syncthreads();
-      // row segments: 2 WN 16-byte pieces per row, 64 rows
-      constexpr int PIECES = 64 * 2 * WN;
+      const int t = threadIdx.x;
+      uint8_t* out = (uint8_t*)sg.out + sg.col0 + 32 * panel0;
 #pragma unroll
-      for (int q = 0; q < PIECES / 64; ++q) {
-        const int id = q * 64 + ln;
-        const int lr = id / (2 * WN), piece = id % (2 * WN);
-        const int row = mb + 16 * ((lr >> 4) * WM + pm) + (lr & 15);
-        if (row < r1 && piece < 2 * npan) {
-          const u32x4 v = *(const u32x4*)(stg + lr * 32 * WN + 16 * piece);
-          *(u32x4*)((uint8_t*)sg.out + (int64_t)row * sg.ldo + sg.col0 + 32 * panel0 + 16 * piece) = v;
-        }
+      for (int q = 0; q < ROWS / 32; ++q) {
+        const int lr = 32 * q + t / 8, piece = t % 8;
+        if (lr < nrow && piece < 2 * npan)
+          *(u32x4*)(out + (int64_t)(mb + lr) * sg.ldo + 16 * piece) = *(const u32x4*)(stg + lr * 128 + 16 * piece);
       }
-      {
-        const int lr = ln;
-        const int row = mb + 16 * ((lr >> 4) * WM + pm) + (lr & 15);
-        if (row < r1) {
-          for (int p = 0; p < npan; ++p)
-            sg.out_scales[(int64_t)row * sg.ldos + (sg.col0 + 32 * panel0) / 32 + p] = stg_sc[lr * WN + p];
-        }
+      if (t < nrow) {
+        uint8_t* os = sg.out_scales + (int64_t)(mb + t) * sg.ldos + sg.col0 / 32 + panel0;
+        if (npan == 4)
+          *(u32*)os = *(const u32*)(stg_sc + 4 * t);
+        else
+          for (int p = 0; p < npan; ++p) os[p] = stg_sc[4 * t + p];
       }
     } else {
+      const rsrc_t orr = make_rsrc((float*)sg.out + (int64_t)mb * sg.ldo + sg.col0, (int64_t)nrow * sg.ldo * 4);
+#pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        if (!ton[mt]) continue;
-        for (int p = 0; p < npan; ++p) {
-          f32x4 tile[4];
 #pragma unroll
-          for (int m2 = 0; m2 < MT; ++m2)
+        for (int ct = 0; ct < 4; ++ct) {
+          const int col = 64 * (panel0 + pm) + 16 * ct + ej;
 #pragma unroll
-            for (int p2 = 0; p2 < WN; ++p2)
-              if (m2 == mt && p2 == p) {
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) tile[rt] = acc[m2][4 * p2 + rt];
-              }
-          epilogue(args, tile, panel0 + p, mb + 16 * (mt * WM + pm), r1, lane);
+          for (int r = 0; r < 4; ++r) {
+            const int lr = 16 * mt + 4 * eg + r;
+            const bool ok = lr < nrow && pok && col < sg.ncols;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mt][ct][r]), orr,
+                                                  ok ? 4 * (lr * (int)sg.ldo + col) : kOOB, 0, 0);
+          }
         }
       }
     }
@@ -866,11 +778,24 @@ static void launch_one(GemmArgs a, hipStream_t s) {
                      0, s, a);
 }
 
-template <int TAG>
+// The scaled-MFMA grouped kernel takes grouped launches with many rows per group, whole K windows,
+// 16-byte aligned activation rows, 4-byte aligned scale rows and one epilogue segment of the given
+// mode (GLU output rows 16-byte aligned, scale rows 4-byte aligned at panel-block granularity).
+static bool f8_grouped_ok(const GemmArgs& a, int mode) {
+  if (!a.many_rows || !a.offsets || a.a_fmt != A_MXFP8 || a.K % kWinK || a.lda % 16 || a.ldas % 4) return false;
+  if (a.nseg != 1 || a.seg[0].p0 != 0 || a.seg[0].p1 < a.P || a.seg[0].mode != mode) return false;
+  const EpiSeg& sg = a.seg[0];
+  if (mode == EPI_SWIGLU_MXFP8)
+    return sg.ldo % 16 == 0 && sg.col0 % 128 == 0 && sg.ldos % 4 == 0 && sg.ncols == 32 * a.P;
+  return true;
+}
+
+template <int EPI, int TAG>
 static void launch_f8(const GemmArgs& a, hipStream_t s) {
-  constexpr int WN = 4, WM = 4, DA = 2, DB = 2;
-  dim3 grid((unsigned)ceil_div(a.P, WN), a.offsets ? (unsigned)a.n_groups : (unsigned)ceil_div(a.M, 64 * WM));
-  hipLaunchKernelGGL((grouped_f8_kernel<WN, WM, DA, DB, TAG>), grid, dim3(64 * WM), 0, s, a);
+  constexpr int D = 3;
+  const unsigned nblk = (unsigned)ceil_div(a.P, 4);
+  const unsigned g8 = (unsigned)ceil_div(a.n_groups, 8) * 8;
+  hipLaunchKernelGGL((grouped_f8_kernel<D, EPI, TAG>), dim3(g8 * nblk), dim3(256), 0, s, a);
 }
 
 hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) {
@@ -886,16 +811,16 @@ hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) 
     case GEMM_GATEUP:
       if (a.a_fmt == A_BF16)
         launch_one<1, A_BF16, 3, 1, true, GEMM_GATEUP>(a, s);
-      else if (a.many_rows)
-        launch_f8<GEMM_GATEUP>(a, s);
+      else if (f8_grouped_ok(a, EPI_SWIGLU_MXFP8))
+        launch_f8<1, GEMM_GATEUP>(a, s);
       else
         launch_one<1, A_MXFP8, 3, 1, true, GEMM_GATEUP>(a, s);
       break;
     case GEMM_DOWN:
       if (a.a_fmt == A_BF16)
         launch_one<1, A_BF16, 3, 1, true, GEMM_DOWN>(a, s);
-      else if (a.many_rows)
-        launch_f8<GEMM_DOWN>(a, s);
+      else if (f8_grouped_ok(a, EPI_F32))
+        launch_f8<0, GEMM_DOWN>(a, s);
       else
         launch_one<1, A_MXFP8, 3, 1, true, GEMM_DOWN>(a, s);
       break;

@@ -2,7 +2,8 @@
 
 Sizes: tiny LatentMoE (T = 64, d = 256, l = 128, hidden 96, E = 16, k = 4, one shared expert)
 and variants (MXFP8 activations, full-width conventional MoE, skewed bias with two shared
-experts); ragged token counts 1..63 cover partial 16-row tiles.
+experts, MXFP8 with many rows per expert over several K windows and row chunks); ragged token
+counts cover partial 16-row tiles and partial row chunks.
 """
 from __future__ import annotations
 
@@ -129,7 +130,8 @@ def check_all(name, T):
     return g
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_mxfp8", "tiny_mxfp8_many", "tiny_fullwidth", "tiny_skewed"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_mxfp8", "tiny_mxfp8_many", "tiny_mxfp8_deep", "tiny_fullwidth",
+                                  "tiny_skewed"])
 def test_full_parity(name):
     check_all(name, workloads.get(name).T)
 
@@ -147,6 +149,12 @@ def test_mxfp8_ragged():
 def test_mxfp8_many_rows_ragged(T):
     """Scaled-MFMA grouped kernel: expert row counts that leave partial 16-row tiles and chunks."""
     check_all("tiny_mxfp8_many", T)
+
+
+@pytest.mark.parametrize("T", [1, 255, 777])
+def test_mxfp8_deep_ragged(T):
+    """Scaled-MFMA grouped kernel over several K windows and several 256-row chunks per expert."""
+    check_all("tiny_mxfp8_deep", T)
 
 
 def test_deterministic_and_stream_order():

@@ -200,6 +200,11 @@ WORKLOADS = {
     "tiny_mxfp8_many": Workload("tiny_mxfp8_many", LayerShape(d=256, l=128, h=128, E=16, k=4, Ns=1, hs=96,
                                                               act="mxfp8"), T=512, seed=0,
                                 note="tiny layer, MXFP8, 128 rows per expert (scaled-MFMA grouped kernel)"),
+    "tiny_mxfp8_deep": Workload("tiny_mxfp8_deep", LayerShape(d=256, l=640, h=768, E=16, k=4, Ns=1, hs=64,
+                                                              act="mxfp8"), T=1024, seed=7, bias="zipf",
+                                zipf_alpha=0.2,
+                                note="tiny layer, MXFP8, several K windows, skewed rows per expert (some above "
+                                     "256: several row chunks)"),
     "tiny_fullwidth": Workload("tiny_fullwidth", LayerShape(d=256, l=256, h=96, E=16, k=2, Ns=1, hs=96,
                                                             latent_moe=0), T=64, seed=5,
                                note="tiny conventional full-width MoE"),
