@@ -508,39 +508,51 @@ __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_ker
 // ---------------------------------------------------------------------------------------------
 typedef int i32x8 __attribute__((__vector_size__(8 * sizeof(int))));
 
-struct F8Tile {
-  u32x4 lo, hi;  // K bytes [16 g, +16) and [64 + 16 g, +16) of the lane's row
-  u32 sc;        // E8M0 of (row, K block g)
-};
 
-// LDS-DMA of 16 / 4 bytes per lane (lane l's data lands at lds + 16 l / 4 l); default cache policy,
-// so the activation rows stay in L2 for the other panel blocks of the group.
-__device__ __forceinline__ void lds_dma16(rsrc_t r, uint8_t* lds, int off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+// LDS-DMA (buffer_load ... lds) of 16 / 4 bytes per lane: lane l's data lands at LDS address
+// lds + 16 l / lds + 4 l. Issued from asm, so the compiler neither orders its own LDS reads behind
+// these writes (the kernel's explicit vmcnt wait and barrier order them) nor reuses M0 across
+// them (M0, which holds the LDS address, is saved and restored). The resource is four SGPRs:
+// base, stride 0, byte count, raw-buffer word 3. Default cache policy: the activation rows stay
+// in L2 for the other panel blocks of the group.
+typedef int i32x4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4s sgpr_rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  i32x4s r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));  // stride 0
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = kRsrcWord3;
+  return r;
 }
-__device__ __forceinline__ void lds_dma4(rsrc_t r, uint8_t* lds, int off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, off, 0, 0, 0);
+__device__ __forceinline__ u32 lds_addr(const void* p) {
+  return (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
-
-// An fp8 A operand from an LDS stage: the two 16-byte halves and the scale byte, with the tile's
-// offsets inside the stage as instruction immediates (one base register per operand part serves
-// every row tile). Written as asm so that the compiler does not order these reads after every LDS
-// DMA still in flight (the caller's vmcnt wait and barrier already guarantee the stage has
-// landed, while the DMAs of later stages keep streaming). The reads and their lgkmcnt wait are
-// one asm statement: were they split, the compiler could copy the destination registers (to
-// form the 8-register MFMA operand) between the issue and the wait, before the data arrives.
-// The MFMAs already issued keep the matrix core busy while the wave waits here.
-template <int LO, int HI, int SC>
-__device__ __forceinline__ void lds_read_atile_at(u32 lo_a, u32 hi_a, u32 sc_a, u32x4& lo, u32x4& hi, u32& sc) {
-  static_assert(LO < 65536 && HI < 65536 && SC < 65536, "ds offset range");
+template <int LDS_OFF>
+__device__ __forceinline__ void dma16(i32x4s r, u32 lds, int voff) {
+  int m0save;
   asm volatile(
-      "ds_read_b128 %0, %3 offset:%6\n\t"
-      "ds_read_b128 %1, %4 offset:%7\n\t"
-      "ds_read_u8 %2, %5 offset:%8\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=v"(lo), "=v"(hi), "=v"(sc)
-      : "v"(lo_a), "v"(hi_a), "v"(sc_a), "i"(LO), "i"(HI), "i"(SC)
-      : "memory");
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %1, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0save)
+      : "s"(lds), "v"(voff), "s"(r), "i"(LDS_OFF)
+      : "memory", "scc");
+}
+template <int LDS_OFF>
+__device__ __forceinline__ void dma4(i32x4s r, u32 lds, int voff) {
+  int m0save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %1, %4\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0save)
+      : "s"(lds), "v"(voff), "s"(r), "i"(LDS_OFF)
+      : "memory", "scc");
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -550,27 +562,44 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barrier that is also a compiler memory barrier, without the cache waits of
+// __syncthreads (no memory operation moves across it; the caller's explicit waits order the DMAs).
+__device__ __forceinline__ void barrier_nowait() { asm volatile("s_barrier" ::: "memory"); }
+
 // Grouped MXFP8 x MXFP4 GEMM on the scaled MFMA, for groups with many rows (prefill).
 // Block: 4 waves on one group (expert) and 4 consecutive panels; wave pm owns panel panel0 + pm for
-// a chunk of up to 256 of the group's rows (16 row tiles x 4 column tiles of 16x16, fp32
-// accumulators). Per K window of 128:
-//   - the chunk's activation rows (E4M3 codes, E8M0 scales) are DMA'd into an LDS stage shared by
-//     the four waves, D windows ahead (16-byte chunk c of row r stored at position c ^ (r & 7));
-//   - each wave streams its own panel-window of weights into registers, D windows ahead;
-//   - one v_mfma_scale_f32_16x16x128_f8f6f4 per (row tile with rows, column tile).
+// a chunk of up to ROWS of the group's rows (MT row tiles x 4 column tiles of 16x16, fp32
+// accumulators). Per K window of 128, by LDS-DMA (buffer_load ... lds) issued from asm:
+//   - the chunk's activation rows (E4M3 codes, E8M0 scales) into an A stage shared by the four
+//     waves, DA windows ahead (16-byte chunk c of row r stored at position c ^ (r & 7));
+//   - each wave's own panel-window of weights into a B stage, DB windows ahead (the weights come
+//     from HBM, the activation rows mostly from L2, hence the deeper weight ring).
+// Nothing in the loop is a compiler-visible global load: one explicit vmcnt wait and a barrier per
+// window order the DMAs, and the operands are plain LDS reads that the compiler places straight
+// into the MFMA operand registers. One v_mfma_scale_f32_16x16x128_f8f6f4 per (row tile with rows,
+// column tile).
 // Blocks are dealt to the XCDs so that every panel block of a group runs on the XCD of that group
 // (group g on XCD g mod 8): the group's activation rows are fetched into one L2 and re-read there.
 // EPI 0: fp32 out. EPI 1: GLU panels, SiLU(gate) * up MX-encoded (E4M3, E8M0 per 32 units),
 // staged in LDS and written as 16-byte row segments.
-template <int D, int EPI, int TAG>
+template <int DA, int DB, int MT, int EPI, int TAG>
 __global__ __launch_bounds__(256) void grouped_f8_kernel(GemmArgs args) {
-  constexpr int MT = 16, ROWS = 256, NA = D + 1, NBR = D + 1;
+  constexpr int ROWS = 16 * MT, NA = DA + 1, NB = DB + 1;
   constexpr int A_SC = ROWS * 128;
-  constexpr int A_STAGE = A_SC + ROWS * 4;
-  constexpr int APW = ROWS / 8 / 4;  // 1 KB code DMAs per wave and window (8 rows each)
-  constexpr int LPW = APW + 1 + 5;   // + one scale DMA (64 rows) + five weight loads
-  static_assert((D - 1) * LPW < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(16))) uint8_t asm_[NA][A_STAGE];
+  constexpr int A_STAGE = A_SC + 4 * 256;     // scale rows padded to four waves' 64 rows
+  constexpr int B_STAGE = 4 * kPanelWinBytes; // one panel-window per wave
+  constexpr int APW = ROWS / 32;              // 1 KB code DMAs per wave and window (8 rows each)
+  constexpr int AL = APW + 1;                 // + one scale DMA (64 rows)
+  constexpr int BL = 5;                       // four 1 KB code DMAs + one 256 B scale DMA
+  constexpr int LPW = AL + BL;
+  static_assert(ROWS % 32 == 0 && ROWS <= 256 && DB >= DA && DA >= 1, "shape");
+  // at step w, A(w) is followed by B(w + DB - DA) and DA - 1 full steps
+  constexpr int WAITN = BL + (DA - 1) * LPW;
+  static_assert(WAITN < 64, "vmcnt range");
+  static_assert(EPI == 0 || ROWS * 132 <= A_STAGE, "epilogue staging fits one A stage");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[NA][A_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[NB][B_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sink[1024];
 
   const int lane = threadIdx.x & 63;
   const int pm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -584,12 +613,13 @@ __global__ __launch_bounds__(256) void grouped_f8_kernel(GemmArgs args) {
   const int npan = min(4, args.P - panel0);
   const bool pok = pm < npan;
   const int nwin = args.wwin;
-  const rsrc_t wr = make_rsrc(args.W + (int64_t)grp * args.w_group_stride +
+  const i32x4s wr = sgpr_rsrc(args.W + (int64_t)grp * args.w_group_stride +
                                   (int64_t)(pok ? panel0 + pm : 0) * nwin * kPanelWinBytes,
                               pok ? (int64_t)nwin * kPanelWinBytes : 0);
-  const rsrc_t ar = make_rsrc(args.A, args.a_bytes);
-  const rsrc_t asr = make_rsrc(args.A_scales, args.as_bytes);
+  const i32x4s ar = sgpr_rsrc(args.A, args.a_bytes);
+  const i32x4s asr = sgpr_rsrc(args.A_scales, args.as_bytes);
   const int g = lane >> 4, i16 = lane & 15;
+  const u32 lds_a0 = lds_addr(&lds_a[0][0]), lds_b0 = lds_addr(&lds_b[0][0]), lds_s = lds_addr(lds_sink);
 
   for (int mb = r0; mb < r1; mb += ROWS) {
     // A DMAs of this wave: code instruction j = pm APW + jj covers chunk rows 8 j .. 8 j + 7
@@ -611,26 +641,32 @@ __global__ __launch_bounds__(256) void grouped_f8_kernel(GemmArgs args) {
       const int c = (lane & 7) ^ (r & 7);
       acode[jj] = mb + r < r1 ? acode[jj] * (int)args.lda + 16 * c : -1;
     }
-    ascale = mb + 64 * pm + lane < r1 ? ascale * (int)args.ldas : -1;
+    ascale = 64 * pm + lane < ROWS && mb + 64 * pm + lane < r1 ? ascale * (int)args.ldas : -1;
+    const u32 a_w = lds_a0 + 1024 * (pm * APW), a_s = lds_a0 + A_SC + 256 * pm;
+    const u32 b_w = lds_b0 + pm * kPanelWinBytes;
+    // issue_a with w < 0 is a prologue dummy (same instruction count, zeros into the sink), so
+    // that one wait count holds at every step
     auto issue_a = [&](int w) {
-      uint8_t* st = asm_[w % NA];
+      const bool real = w >= 0;
+      const u32 st = real ? a_w + (u32)((w % NA) * A_STAGE) : lds_s;
+      const u32 ss = real ? a_s + (u32)((w % NA) * A_STAGE) : lds_s;
+      const bool in = real && w < nwin;
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        (dma16<0>(ar, real ? st + 1024 * J : st, in && acode[J] >= 0 ? acode[J] + 128 * w : kOOB), ...);
+      }(std::make_integer_sequence<int, APW>{});
+      dma4<0>(asr, ss, in && ascale >= 0 ? ascale + 4 * w : kOOB);
+    };
+    auto issue_b = [&](int w) {
+      const u32 st = b_w + (u32)((w % NB) * B_STAGE);
       const bool in = w < nwin;
-#pragma unroll
-      for (int jj = 0; jj < APW; ++jj)
-        lds_dma16(ar, st + 1024 * (pm * APW + jj), in && acode[jj] >= 0 ? acode[jj] + 128 * w : kOOB);
-      lds_dma4(asr, st + A_SC + 256 * pm, in && ascale >= 0 ? ascale + 4 * w : kOOB);
+      const int v = lane * 16 + w * kPanelWinBytes;
+      dma16<0>(wr, st, in ? v : kOOB);
+      dma16<0>(wr, st + 1024, in ? v + 1024 : kOOB);
+      dma16<0>(wr, st + 2048, in ? v + 2048 : kOOB);
+      dma16<0>(wr, st + 3072, in ? v + 3072 : kOOB);
+      dma4<0>(wr, st + 4096, in ? lane * 4 + w * kPanelWinBytes + 4096 : kOOB);
     };
-    u32x4 bw[NBR][4];
-    u32 bs[NBR];
-    auto issue_b = [&](int w, u32x4(&c)[4], u32& sc) {
-      const int off = w < nwin ? w * kPanelWinBytes : kOOB;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-        c[rt] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + rt * 1024 + lane * 16, 0, kNT);
-      sc = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 4096 + lane * 4, 0, kNT);
-    };
-    // row tiles holding rows (uniform)
-    const int nt = min(MT, (r1 - mb + 15) / 16);
+    const int nt = min(MT, (r1 - mb + 15) / 16);  // row tiles holding rows (uniform)
 
     f32x4 acc[MT][4];
 #pragma unroll
@@ -638,56 +674,50 @@ __global__ __launch_bounds__(256) void grouped_f8_kernel(GemmArgs args) {
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-      issue_a(i);
-      issue_b(i, bw[i], bs[i]);
-    }
-    for (int w0 = 0; w0 < nwin; w0 += NBR) {
-#pragma unroll
-      for (int u = 0; u < NBR; ++u) {
-        const int w = w0 + u;
-        if (w >= nwin) break;  // uniform
-        // A(w) and B(w) were issued D steps ago, followed by D - 1 steps' worth of loads
-        wait_vmcnt<(D - 1) * LPW>();
-        __builtin_amdgcn_s_barrier();  // stage w complete for every wave; stage w - 1 free
-        issue_a(w + D);
-        issue_b(w + D, bw[(u + D) % NBR], bs[(u + D) % NBR]);
-        // A operands: row tile mt of the stage sits at mt * 2048 (codes) and A_SC + mt * 64 (scales);
-        // the swizzle depends on the row only through row % 8 = i16 % 8.
-        const u32 sbase = (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)asm_[w % NA];
-        const u32 lo_a = sbase + i16 * 128 + 16 * (g ^ (i16 & 7));
-        const u32 hi_a = sbase + i16 * 128 + 16 * ((4 + g) ^ (i16 & 7));
-        const u32 sc_a = sbase + i16 * 4 + g;
-        F8Tile cur;
-        lds_read_atile_at<0, 0, A_SC>(lo_a, hi_a, sc_a, cur.lo, cur.hi, cur.sc);
-        // one body per row tile (compile-time mt: immediates, static accumulator indices); tiles
-        // past the chunk's rows are skipped (uniform). The next tile's operands are read while
-        // this tile's four MFMAs run.
-        [&]<int... MTI>(std::integer_sequence<int, MTI...>) {
-          ([&] {
-            constexpr int mt = MTI;
-            if (mt < nt) {
-              const i32x8 aop = {(int)cur.lo[0], (int)cur.lo[1], (int)cur.lo[2], (int)cur.lo[3],
-                                 (int)cur.hi[0], (int)cur.hi[1], (int)cur.hi[2], (int)cur.hi[3]};
-              const int asc = (int)cur.sc;
-#pragma unroll
-              for (int ct = 0; ct < 4; ++ct) {
-                const i32x8 bop = {(int)bw[u][ct][0], (int)bw[u][ct][1], (int)bw[u][ct][2], (int)bw[u][ct][3],
-                                   0, 0, 0, 0};
-                acc[mt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc[mt][ct], 0, 4, 0, asc, 0,
-                                                                                (int)(bs[u] >> (8 * ct)));
-              }
-              if constexpr (mt + 1 < MT) {
-                if (mt + 1 < nt)
-                  lds_read_atile_at<(mt + 1) * 2048, (mt + 1) * 2048, A_SC + (mt + 1) * 64>(lo_a, hi_a, sc_a, cur.lo,
-                                                                                           cur.hi, cur.sc);
-              }
-            }
-          }(), ...);
-        }(std::make_integer_sequence<int, MT>{});
+    // The window loop, specialised on the number of row tiles holding rows (one variant per count,
+    // chosen once per chunk) so that each window's body is straight-line code: the compiler can
+    // interleave the LDS reads of later tiles with the MFMAs of earlier ones.
+    auto run = [&]<int N>() {
+      // prologue in steady-state order: step i issues A(i + DA), then B(i + DB)
+      for (int i = -DB; i < 0; ++i) {
+        issue_a(i + DA);
+        issue_b(i + DB);
       }
-    }
+      for (int w = 0; w < nwin; ++w) {
+        wait_vmcnt<WAITN>();
+        barrier_nowait();  // stages of w complete for every wave; stages of w - 1 free
+        issue_a(w + DA);
+        issue_b(w + DB);
+        // weights of this wave's panel-window
+        const uint8_t* sb = &lds_b[w % NB][pm * kPanelWinBytes];
+        u32x4 bw[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) bw[rt] = *(const u32x4*)(sb + rt * 1024 + lane * 16);
+        const u32 bsc = *(const u32*)(sb + 4096 + lane * 4);
+        // A operands: row tile mt of the stage has its codes at mt * 2048 and scales at
+        // A_SC + mt * 64; the swizzle depends on the row only through row % 8 = i16 % 8
+        const uint8_t* sa = lds_a[w % NA];
+        const uint8_t* plo = sa + i16 * 128 + 16 * (g ^ (i16 & 7));
+        const uint8_t* phi = sa + i16 * 128 + 16 * ((4 + g) ^ (i16 & 7));
+        const uint8_t* psc = sa + A_SC + i16 * 4 + g;
+#pragma unroll
+        for (int mt = 0; mt < N; ++mt) {
+          const u32x4 lo = *(const u32x4*)(plo + mt * 2048);
+          const u32x4 hi = *(const u32x4*)(phi + mt * 2048);
+          const int asc = psc[mt * 64];
+          const i32x8 aop = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const i32x8 bop = {(int)bw[ct][0], (int)bw[ct][1], (int)bw[ct][2], (int)bw[ct][3], 0, 0, 0, 0};
+            acc[mt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc[mt][ct], 0, 4, 0, asc, 0,
+                                                                            (int)(bsc >> (8 * ct)));
+          }
+        }
+      }
+    };
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((nt == I + 1 ? (run.template operator()<I + 1>(), 0) : 0), ...);
+    }(std::make_integer_sequence<int, MT>{});
     wait_vmcnt<0>();
     __syncthreads();  // rings idle
 
@@ -699,8 +729,8 @@ __global__ __launch_bounds__(256) void grouped_f8_kernel(GemmArgs args) {
     const EpiSeg& sg = args.seg[0];
     const int nrow = min(ROWS, r1 - mb);
     if constexpr (EPI == 1) {
-      // codes staged as [256 rows][128 bytes] (32 units per panel), scales as [256 rows][4]
-      uint8_t* stg = &asm_[0][0];
+      // codes staged as [ROWS][128 bytes] (32 units per panel), scales as [ROWS][4]
+      uint8_t* stg = &lds_a[0][0];
       uint8_t* stg_sc = stg + ROWS * 128;
       const bool tap = sg.pre != nullptr;
       const rsrc_t prr = make_rsrc(tap ? sg.pre + (int64_t)mb * sg.ldpre : nullptr,
@@ -792,10 +822,10 @@ static bool f8_grouped_ok(const GemmArgs& a, int mode) {
 
 template <int EPI, int TAG>
 static void launch_f8(const GemmArgs& a, hipStream_t s) {
-  constexpr int D = 3;
+  constexpr int DA = 2, DB = 3, MT = 12;
   const unsigned nblk = (unsigned)ceil_div(a.P, 4);
   const unsigned g8 = (unsigned)ceil_div(a.n_groups, 8) * 8;
-  hipLaunchKernelGGL((grouped_f8_kernel<D, EPI, TAG>), dim3(g8 * nblk), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((grouped_f8_kernel<DA, DB, MT, EPI, TAG>), dim3(g8 * nblk), dim3(256), 0, s, a);
 }
 
 hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) {
