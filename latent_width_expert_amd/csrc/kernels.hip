@@ -36,29 +36,31 @@ __device__ __forceinline__ u32 bf16_rne(float f) {
 // E4M3 ("fn") code of x (already divided by its block scale): round to nearest even on the
 // E4M3 grid, saturate at 448, keep the sign (also of a zero result).
 __device__ __forceinline__ u32 e4m3_code(float x) {
-  u32 sign = (__float_as_uint(x) >> 24) & 0x80u;
-  float a = fabsf(x);
-  u32 code;
-  if (a < 0x1p-6f) {
-    code = (u32)rintf(a * 512.0f);  // subnormal grid step 2^-9; 8 steps = smallest normal (code 8)
-  } else {
-    u32 b = __float_as_uint(a);
-    b = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;  // keep 3 mantissa bits, ties to even
-    float r = fminf(__uint_as_float(b), 448.0f);
-    b = __float_as_uint(r);
-    code = ((((b >> 23) & 0xFFu) - 127u + 7u) << 3) | ((b >> 20) & 7u);
-  }
-  return sign | code;
+  // both ranges computed and one selected: no divergent branch per element
+  const u32 sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  const u32 sub = (u32)rintf(a * 512.0f);  // subnormal grid step 2^-9; 8 steps = smallest normal (code 8)
+  u32 b = __float_as_uint(a);
+  b = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;  // keep 3 mantissa bits, ties to even
+  b = __float_as_uint(fminf(__uint_as_float(b), 448.0f));
+  const u32 nrm = ((((b >> 23) & 0xFFu) - 120u) << 3) | ((b >> 20) & 7u);
+  return sign | (a < 0x1p-6f ? sub : nrm);
 }
 
 // E8M0 byte of an MX block with largest magnitude amax > 0 for an element format whose largest
 // binade starts at 2^emax: exponent floor(log2 amax) - emax, clamped to [-127, 127].
 __device__ __forceinline__ int mx_shared_exp(float amax, int emax) {
-  int e = ilogbf(amax) - emax;
+  // frexp exponent: amax = m 2^x with m in [0.5, 1), so floor(log2 amax) = x - 1 (denormals included)
+  const int e = __builtin_amdgcn_frexp_expf(amax) - 1 - emax;
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+// SiLU(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal (about one ulp each); a gate
+// below about -88 gives e^-g = inf and SiLU = -0.
+__device__ __forceinline__ float silu(float g) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // Raw buffer loads: the hardware bounds-checks every load against the resource's byte count and
 // returns zeros for out-of-range offsets without touching memory, so tails and masked lanes need
@@ -258,14 +260,8 @@ __device__ __forceinline__ float row16_max(float v) {
 // one lane group; returns the E4M3 codes of v0, v1 and the E8M0 byte. All 64 lanes must call.
 __device__ __forceinline__ void mxfp8_block(float v0, float v1, u32& c0, u32& c1, u32& sbyte) {
   const float amax = row16_max(fmaxf(fabsf(v0), fabsf(v1)));
-  if (amax == 0.0f) {
-    sbyte = 0;
-    c0 = (__float_as_uint(v0) >> 24) & 0x80u;
-    c1 = (__float_as_uint(v1) >> 24) & 0x80u;
-    return;
-  }
   const int e = mx_shared_exp(amax, 8);
-  sbyte = (u32)(e + 127);
+  sbyte = amax == 0.0f ? 0u : (u32)(e + 127);  // an all-zero block: scale byte 0, codes +-0
   const float inv = e8m0_f32((u32)(127 - e));  // 2^-e
   c0 = e4m3_code(v0 * inv);
   c1 = e4m3_code(v1 * inv);
@@ -513,8 +509,8 @@ typedef int i32x8 __attribute__((__vector_size__(8 * sizeof(int))));
 // lds + 16 l / lds + 4 l. Issued from asm, so the compiler neither orders its own LDS reads behind
 // these writes (the kernel's explicit vmcnt wait and barrier order them) nor reuses M0 across
 // them (M0, which holds the LDS address, is saved and restored). The resource is four SGPRs:
-// base, stride 0, byte count, raw-buffer word 3. Default cache policy: the activation rows stay
-// in L2 for the other panel blocks of the group.
+// base, stride 0, byte count, raw-buffer word 3. NT: non-temporal (streamed weights); otherwise
+// the default policy (activation rows stay in L2 for the other panel blocks of the group).
 typedef int i32x4s __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4s sgpr_rsrc(const void* base, int64_t bytes) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
@@ -528,31 +524,53 @@ __device__ __forceinline__ i32x4s sgpr_rsrc(const void* base, int64_t bytes) {
 __device__ __forceinline__ u32 lds_addr(const void* p) {
   return (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
-template <int LDS_OFF>
+template <bool NT>
 __device__ __forceinline__ void dma16(i32x4s r, u32 lds, int voff) {
   int m0save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_add_u32 m0, %1, %4\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(m0save)
-      : "s"(lds), "v"(voff), "s"(r), "i"(LDS_OFF)
-      : "memory", "scc");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0save)
+        : "s"(lds), "v"(voff), "s"(r)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0save)
+        : "s"(lds), "v"(voff), "s"(r)
+        : "memory");
 }
-template <int LDS_OFF>
+template <bool NT>
 __device__ __forceinline__ void dma4(i32x4s r, u32 lds, int voff) {
   int m0save;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_add_u32 m0, %1, %4\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dword %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(m0save)
-      : "s"(lds), "v"(voff), "s"(r), "i"(LDS_OFF)
-      : "memory", "scc");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %2, %3, 0 offen nt lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0save)
+        : "s"(lds), "v"(voff), "s"(r)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0save)
+        : "s"(lds), "v"(voff), "s"(r)
+        : "memory");
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -567,13 +585,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void barrier_nowait() { asm volatile("s_barrier" ::: "memory"); }
 
 // Grouped MXFP8 x MXFP4 GEMM on the scaled MFMA, for groups with many rows (prefill).
-// Block: 4 waves on one group (expert) and 4 consecutive panels; wave pm owns panel panel0 + pm for
-// a chunk of up to ROWS of the group's rows (MT row tiles x 4 column tiles of 16x16, fp32
-// accumulators). Per K window of 128, by LDS-DMA (buffer_load ... lds) issued from asm:
-//   - the chunk's activation rows (E4M3 codes, E8M0 scales) into an A stage shared by the four
-//     waves, DA windows ahead (16-byte chunk c of row r stored at position c ^ (r & 7));
-//   - each wave's own panel-window of weights into a B stage, DB windows ahead (the weights come
-//     from HBM, the activation rows mostly from L2, hence the deeper weight ring).
+// Block: 4 WPS waves on one group (expert) and 4 consecutive panels, WPS waves per SIMD. Wave
+// (pm, h) computes panel panel0 + pm on the row tiles h, h + WPS, ... of a chunk of up to ROWS of
+// the group's rows (4 column tiles of 16x16 per row tile, fp32 accumulators); with two waves per
+// SIMD one wave's MFMAs run while the other waits on LDS or on its DMA issues. Per K window of
+// 128, by LDS-DMA (buffer_load ... lds) issued from asm:
+//   - the chunk's activation rows (E4M3 codes, E8M0 scales) into an A stage shared by all waves,
+//     DA windows ahead (16-byte chunk c of row r stored at position c ^ (r & 7));
+//   - each panel-window of weights into a B stage, DB windows ahead, non-temporal (the weights
+//     come from HBM, the activation rows mostly from L2, hence the deeper weight ring).
 // Nothing in the loop is a compiler-visible global load: one explicit vmcnt wait and a barrier per
 // window order the DMAs, and the operands are plain LDS reads that the compiler places straight
 // into the MFMA operand registers. One v_mfma_scale_f32_16x16x128_f8f6f4 per (row tile with rows,
@@ -582,27 +602,31 @@ __device__ __forceinline__ void barrier_nowait() { asm volatile("s_barrier" ::: 
 // (group g on XCD g mod 8): the group's activation rows are fetched into one L2 and re-read there.
 // EPI 0: fp32 out. EPI 1: GLU panels, SiLU(gate) * up MX-encoded (E4M3, E8M0 per 32 units),
 // staged in LDS and written as 16-byte row segments.
-template <int DA, int DB, int MT, int EPI, int TAG>
-__global__ __launch_bounds__(256) void grouped_f8_kernel(GemmArgs args) {
+template <int DA, int DB, int MT, int WPS, int EPI, int TAG>
+__global__ __launch_bounds__(256 * WPS) void grouped_f8_kernel(GemmArgs args) {
+  constexpr int NWAVE = 4 * WPS;                // WPS waves per SIMD
   constexpr int ROWS = 16 * MT, NA = DA + 1, NB = DB + 1;
+  constexpr int MTW = MT / WPS;                 // row tiles per wave
   constexpr int A_SC = ROWS * 128;
-  constexpr int A_STAGE = A_SC + 4 * 256;     // scale rows padded to four waves' 64 rows
-  constexpr int B_STAGE = 4 * kPanelWinBytes; // one panel-window per wave
-  constexpr int APW = ROWS / 32;              // 1 KB code DMAs per wave and window (8 rows each)
-  constexpr int AL = APW + 1;                 // + one scale DMA (64 rows)
-  constexpr int BL = 5;                       // four 1 KB code DMAs + one 256 B scale DMA
-  constexpr int LPW = AL + BL;
-  static_assert(ROWS % 32 == 0 && ROWS <= 256 && DB >= DA && DA >= 1, "shape");
-  // at step w, A(w) is followed by B(w + DB - DA) and DA - 1 full steps
-  constexpr int WAITN = BL + (DA - 1) * LPW;
+  constexpr int A_STAGE = A_SC + NWAVE * 256;   // one 256-byte scale slot per wave (64 rows)
+  constexpr int B_STAGE = 4 * kPanelWinBytes;   // one panel-window per panel
+  constexpr int APW = ROWS / 8 / NWAVE;         // 1 KB code DMAs per wave and window (8 rows each)
+  constexpr int AL = APW + 1;                   // + the wave's scale DMA
+  constexpr int BPW = (5 + WPS - 1) / WPS;      // a panel's five weight DMAs over its WPS waves
+  constexpr int LPW = AL + BPW;
+  static_assert(MT % WPS == 0 && (ROWS / 8) % NWAVE == 0 && ROWS <= 64 * NWAVE, "shape");
+  static_assert(DB >= DA && DA >= 1, "ring depths");
+  // at step w, A(w) is followed by the B DMAs of the same step and DA - 1 full steps
+  constexpr int WAITN = BPW + (DA - 1) * LPW;
   static_assert(WAITN < 64, "vmcnt range");
   static_assert(EPI == 0 || ROWS * 132 <= A_STAGE, "epilogue staging fits one A stage");
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[NA][A_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[NB][B_STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_sink[1024];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sink[NWAVE][256];
 
   const int lane = threadIdx.x & 63;
-  const int pm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pm = wv & 3, h = wv >> 2;           // panel of the wave, its row-tile phase
   const int nblk = (args.P + 3) / 4;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int grp = xcd + 8 * (slot / nblk);
@@ -619,105 +643,135 @@ __global__ __launch_bounds__(256) void grouped_f8_kernel(GemmArgs args) {
   const i32x4s ar = sgpr_rsrc(args.A, args.a_bytes);
   const i32x4s asr = sgpr_rsrc(args.A_scales, args.as_bytes);
   const int g = lane >> 4, i16 = lane & 15;
-  const u32 lds_a0 = lds_addr(&lds_a[0][0]), lds_b0 = lds_addr(&lds_b[0][0]), lds_s = lds_addr(lds_sink);
+  const u32 lds_a0 = lds_addr(&lds_a[0][0]), lds_b0 = lds_addr(&lds_b[0][0]);
+  const u32 lds_s = lds_addr(&lds_sink[wv][0]);
 
   for (int mb = r0; mb < r1; mb += ROWS) {
-    // A DMAs of this wave: code instruction j = pm APW + jj covers chunk rows 8 j .. 8 j + 7
+    // A DMAs of this wave: code instruction j = wv APW + jj covers chunk rows 8 j .. 8 j + 7
     // (lane L: row 8 j + L / 8, position L % 8 holding chunk (L % 8) ^ (row & 7)); the scale
-    // instruction covers rows 64 pm .. 64 pm + 63 (lane L: row 64 pm + L).
+    // instruction covers rows 64 wv .. 64 wv + 63 (lane L: row 64 wv + L), zeros past the chunk.
     int acode[APW], ascale;
 #pragma unroll
     for (int jj = 0; jj < APW; ++jj) {
-      const int row = mb + 8 * (pm * APW + jj) + (lane >> 3);
+      const int row = mb + 8 * (wv * APW + jj) + (lane >> 3);
       acode[jj] = args.rowmap ? args.rowmap[min(row, r1 - 1)] : row;
     }
     {
-      const int row = mb + 64 * pm + lane;
+      const int row = mb + 64 * wv + lane;
       ascale = args.rowmap ? args.rowmap[min(row, r1 - 1)] : row;
     }
 #pragma unroll
     for (int jj = 0; jj < APW; ++jj) {
-      const int r = 8 * (pm * APW + jj) + (lane >> 3);
+      const int r = 8 * (wv * APW + jj) + (lane >> 3);
       const int c = (lane & 7) ^ (r & 7);
       acode[jj] = mb + r < r1 ? acode[jj] * (int)args.lda + 16 * c : -1;
     }
-    ascale = 64 * pm + lane < ROWS && mb + 64 * pm + lane < r1 ? ascale * (int)args.ldas : -1;
-    const u32 a_w = lds_a0 + 1024 * (pm * APW), a_s = lds_a0 + A_SC + 256 * pm;
+    ascale = 64 * wv + lane < ROWS && mb + 64 * wv + lane < r1 ? ascale * (int)args.ldas : -1;
+    const u32 a_w = lds_a0 + 1024 * (wv * APW), a_s = lds_a0 + A_SC + 256 * wv;
     const u32 b_w = lds_b0 + pm * kPanelWinBytes;
-    // issue_a with w < 0 is a prologue dummy (same instruction count, zeros into the sink), so
-    // that one wait count holds at every step
-    auto issue_a = [&](int w) {
-      const bool real = w >= 0;
-      const u32 st = real ? a_w + (u32)((w % NA) * A_STAGE) : lds_s;
-      const u32 ss = real ? a_s + (u32)((w % NA) * A_STAGE) : lds_s;
-      const bool in = real && w < nwin;
-      [&]<int... J>(std::integer_sequence<int, J...>) {
-        (dma16<0>(ar, real ? st + 1024 * J : st, in && acode[J] >= 0 ? acode[J] + 128 * w : kOOB), ...);
-      }(std::make_integer_sequence<int, APW>{});
-      dma4<0>(asr, ss, in && ascale >= 0 ? ascale + 4 * w : kOOB);
-    };
-    auto issue_b = [&](int w) {
-      const u32 st = b_w + (u32)((w % NB) * B_STAGE);
-      const bool in = w < nwin;
-      const int v = lane * 16 + w * kPanelWinBytes;
-      dma16<0>(wr, st, in ? v : kOOB);
-      dma16<0>(wr, st + 1024, in ? v + 1024 : kOOB);
-      dma16<0>(wr, st + 2048, in ? v + 2048 : kOOB);
-      dma16<0>(wr, st + 3072, in ? v + 3072 : kOOB);
-      dma4<0>(wr, st + 4096, in ? lane * 4 + w * kPanelWinBytes + 4096 : kOOB);
-    };
-    const int nt = min(MT, (r1 - mb + 15) / 16);  // row tiles holding rows (uniform)
-
-    f32x4 acc[MT][4];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // The window loop, specialised on the number of row tiles holding rows (one variant per count,
-    // chosen once per chunk) so that each window's body is straight-line code: the compiler can
-    // interleave the LDS reads of later tiles with the MFMAs of earlier ones.
-    auto run = [&]<int N>() {
-      // prologue in steady-state order: step i issues A(i + DA), then B(i + DB)
-      for (int i = -DB; i < 0; ++i) {
-        issue_a(i + DA);
-        issue_b(i + DB);
+    // The LPW DMAs of step w, one by one: the wave's A code DMAs, its A scale DMA, then its share
+    // of the panel's five weight DMAs (items h BPW .. h BPW + BPW - 1 of: four 1 KB code pieces,
+    // the 256-byte scale piece; items past five are 4-byte dummies into the wave's sink), always
+    // in this order so that one wait count holds at every step. Step w fills A stage
+    // (w + DA) % NA and B stage (w + DB) % NB; a stage index below zero in the prologue is a dummy.
+    auto issue_one = [&]<int d>(int w) {
+      if constexpr (d < AL) {
+        const int wa = w + DA;
+        const bool real = wa >= 0;
+        const bool in = real && wa < nwin;
+        const u32 st = (u32)((wa % NA) * A_STAGE);
+        if constexpr (d < APW)
+          dma16<false>(ar, real ? a_w + st + 1024 * d : lds_s, in && acode[d] >= 0 ? acode[d] + 128 * wa : kOOB);
+        else
+          dma4<false>(asr, real ? a_s + st : lds_s, in && ascale >= 0 ? ascale + 4 * wa : kOOB);
+      } else {
+        const int wb = w + DB;
+        const bool in = wb < nwin;
+        const u32 st = b_w + (u32)((wb % NB) * B_STAGE);
+        const int item = h * BPW + (d - AL);  // uniform
+        if (item < 4)
+          dma16<true>(wr, st + 1024 * item, in ? lane * 16 + wb * kPanelWinBytes + 1024 * item : kOOB);
+        else if (item == 4)
+          dma4<true>(wr, st + 4096, in ? lane * 4 + wb * kPanelWinBytes + 4096 : kOOB);
+        else
+          dma4<false>(wr, lds_s, kOOB);
       }
+    };
+    auto issue_range = [&]<int D0, int D1>(int w) {
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        (issue_one.template operator()<D0 + I>(w), ...);
+      }(std::make_integer_sequence<int, D1 - D0>{});
+    };
+    // row tiles holding rows (uniform over the block) and this wave's share: tiles h, h + WPS, ...
+    const int nt = min(MT, (r1 - mb + 15) / 16);
+    const int nw = nt > h ? (nt - h + WPS - 1) / WPS : 0;
+
+    f32x4 acc[MTW][4];
+#pragma unroll
+    for (int j = 0; j < MTW; ++j)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[j][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // The window loop, specialised on the wave's number of row tiles holding rows (one variant per
+    // count, chosen once per chunk) so that each window's body is straight-line code.
+    auto run = [&]<int N>() {
+      // prologue: steps -DB .. -1 issue their DMAs in steady-state order
+      for (int i = -DB; i < 0; ++i) issue_range.template operator()<0, LPW>(i);
       for (int w = 0; w < nwin; ++w) {
         wait_vmcnt<WAITN>();
         barrier_nowait();  // stages of w complete for every wave; stages of w - 1 free
-        issue_a(w + DA);
-        issue_b(w + DB);
-        // weights of this wave's panel-window
+        // weights of the wave's panel-window
         const uint8_t* sb = &lds_b[w % NB][pm * kPanelWinBytes];
         u32x4 bw[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) bw[rt] = *(const u32x4*)(sb + rt * 1024 + lane * 16);
         const u32 bsc = *(const u32*)(sb + 4096 + lane * 4);
-        // A operands: row tile mt of the stage has its codes at mt * 2048 and scales at
-        // A_SC + mt * 64; the swizzle depends on the row only through row % 8 = i16 % 8
+        // A operands: row tile t of the stage has its codes at t * 2048 and scales at A_SC + t * 64;
+        // the swizzle depends on the row only through row % 8 = i16 % 8
         const uint8_t* sa = lds_a[w % NA];
-        const uint8_t* plo = sa + i16 * 128 + 16 * (g ^ (i16 & 7));
-        const uint8_t* phi = sa + i16 * 128 + 16 * ((4 + g) ^ (i16 & 7));
-        const uint8_t* psc = sa + A_SC + i16 * 4 + g;
+        const uint8_t* plo = sa + i16 * 128 + 16 * (g ^ (i16 & 7)) + h * 2048;
+        const uint8_t* phi = sa + i16 * 128 + 16 * ((4 + g) ^ (i16 & 7)) + h * 2048;
+        const uint8_t* psc = sa + A_SC + i16 * 4 + g + h * 64;
+        auto load_tile = [&](int j, i32x8& aop, int& asc) {  // the wave's j-th tile: row tile h + WPS j
+          const u32x4 lo = *(const u32x4*)(plo + j * WPS * 2048);
+          const u32x4 hi = *(const u32x4*)(phi + j * WPS * 2048);
+          asc = psc[j * WPS * 64];
+          aop = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        };
+        // the step's DMAs are spread over the tiles (the wave keeps the matrix core busy while the
+        // memory pipeline drains); the next tile's operands are read before each group of DMAs,
+        // which are compiler barriers for memory operations
+        if constexpr (N == 0) {
+          issue_range.template operator()<0, LPW>(w);
+        } else {
+          i32x8 cur;
+          int csc;
+          load_tile(0, cur, csc);
+          [&]<int... JI>(std::integer_sequence<int, JI...>) {
+            ([&] {
+              constexpr int j = JI;
+              i32x8 nxt;
+              int nsc = 0;
+              if constexpr (j + 1 < N) load_tile(j + 1, nxt, nsc);
 #pragma unroll
-        for (int mt = 0; mt < N; ++mt) {
-          const u32x4 lo = *(const u32x4*)(plo + mt * 2048);
-          const u32x4 hi = *(const u32x4*)(phi + mt * 2048);
-          const int asc = psc[mt * 64];
-          const i32x8 aop = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct) {
-            const i32x8 bop = {(int)bw[ct][0], (int)bw[ct][1], (int)bw[ct][2], (int)bw[ct][3], 0, 0, 0, 0};
-            acc[mt][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc[mt][ct], 0, 4, 0, asc, 0,
-                                                                            (int)(bsc >> (8 * ct)));
-          }
+              for (int ct = 0; ct < 4; ++ct) {
+                const i32x8 bop = {(int)bw[ct][0], (int)bw[ct][1], (int)bw[ct][2], (int)bw[ct][3], 0, 0, 0, 0};
+                acc[j][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur, bop, acc[j][ct], 0, 4, 0, csc, 0,
+                                                                             (int)(bsc >> (8 * ct)));
+              }
+              issue_range.template operator()<j * LPW / N, (j + 1) * LPW / N>(w);
+              if constexpr (j + 1 < N) {
+                cur = nxt;
+                csc = nsc;
+              }
+            }(), ...);
+          }(std::make_integer_sequence<int, N>{});
         }
       }
     };
     [&]<int... I>(std::integer_sequence<int, I...>) {
-      ((nt == I + 1 ? (run.template operator()<I + 1>(), 0) : 0), ...);
-    }(std::make_integer_sequence<int, MT>{});
+      ((nw == I ? (run.template operator()<I>(), 0) : 0), ...);
+    }(std::make_integer_sequence<int, MTW + 1>{});
     wait_vmcnt<0>();
     __syncthreads();  // rings idle
 
@@ -736,12 +790,12 @@ __global__ __launch_bounds__(256) void grouped_f8_kernel(GemmArgs args) {
       const rsrc_t prr = make_rsrc(tap ? sg.pre + (int64_t)mb * sg.ldpre : nullptr,
                                    tap ? (int64_t)nrow * sg.ldpre * 4 : 0);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int j = 0; j < MTW; ++j) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float v0 = silu(acc[mt][0][r]) * acc[mt][1][r];
-          const float v1 = silu(acc[mt][2][r]) * acc[mt][3][r];
-          const int lr = 16 * mt + 4 * eg + r;
+          const float v0 = silu(acc[j][0][r]) * acc[j][1][r];
+          const float v1 = silu(acc[j][2][r]) * acc[j][3][r];
+          const int lr = 16 * (h + WPS * j) + 4 * eg + r;
           if (tap) {
             const int o = lr * (int)sg.ldpre + sg.col0 + 32 * (panel0 + pm) + ej;
             const bool ok = lr < nrow && pok;
@@ -760,30 +814,30 @@ __global__ __launch_bounds__(256) void grouped_f8_kernel(GemmArgs args) {
       const int t = threadIdx.x;
       uint8_t* out = (uint8_t*)sg.out + sg.col0 + 32 * panel0;
 #pragma unroll
-      for (int q = 0; q < ROWS / 32; ++q) {
-        const int lr = 32 * q + t / 8, piece = t % 8;
+      for (int q = 0; q < ROWS / (32 * WPS); ++q) {
+        const int lr = 32 * WPS * q + t / 8, piece = t % 8;
         if (lr < nrow && piece < 2 * npan)
           *(u32x4*)(out + (int64_t)(mb + lr) * sg.ldo + 16 * piece) = *(const u32x4*)(stg + lr * 128 + 16 * piece);
       }
-      if (t < nrow) {
-        uint8_t* os = sg.out_scales + (int64_t)(mb + t) * sg.ldos + sg.col0 / 32 + panel0;
+      for (int lr = t; lr < nrow; lr += 256 * WPS) {
+        uint8_t* os = sg.out_scales + (int64_t)(mb + lr) * sg.ldos + sg.col0 / 32 + panel0;
         if (npan == 4)
-          *(u32*)os = *(const u32*)(stg_sc + 4 * t);
+          *(u32*)os = *(const u32*)(stg_sc + 4 * lr);
         else
-          for (int p = 0; p < npan; ++p) os[p] = stg_sc[4 * t + p];
+          for (int p = 0; p < npan; ++p) os[p] = stg_sc[4 * lr + p];
       }
     } else {
       const rsrc_t orr = make_rsrc((float*)sg.out + (int64_t)mb * sg.ldo + sg.col0, (int64_t)nrow * sg.ldo * 4);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int j = 0; j < MTW; ++j) {
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           const int col = 64 * (panel0 + pm) + 16 * ct + ej;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int lr = 16 * mt + 4 * eg + r;
+            const int lr = 16 * (h + WPS * j) + 4 * eg + r;
             const bool ok = lr < nrow && pok && col < sg.ncols;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[mt][ct][r]), orr,
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][ct][r]), orr,
                                                   ok ? 4 * (lr * (int)sg.ldo + col) : kOOB, 0, 0);
           }
         }
@@ -822,10 +876,10 @@ static bool f8_grouped_ok(const GemmArgs& a, int mode) {
 
 template <int EPI, int TAG>
 static void launch_f8(const GemmArgs& a, hipStream_t s) {
-  constexpr int DA = 2, DB = 3, MT = 12;
+  constexpr int DA = 2, DB = 3, MT = 12, WPS = 2;
   const unsigned nblk = (unsigned)ceil_div(a.P, 4);
   const unsigned g8 = (unsigned)ceil_div(a.n_groups, 8) * 8;
-  hipLaunchKernelGGL((grouped_f8_kernel<DA, DB, MT, EPI, TAG>), dim3(g8 * nblk), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((grouped_f8_kernel<DA, DB, MT, WPS, EPI, TAG>), dim3(g8 * nblk), dim3(256 * WPS), 0, s, a);
 }
 
 hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) {
