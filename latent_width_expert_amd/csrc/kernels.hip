@@ -7,6 +7,7 @@
 
 #include <math.h>
 
+#include <type_traits>
 #include <utility>
 
 namespace k3 {
@@ -584,42 +585,51 @@ __device__ __forceinline__ void wait_vmcnt() {
 // __syncthreads (no memory operation moves across it; the caller's explicit waits order the DMAs).
 __device__ __forceinline__ void barrier_nowait() { asm volatile("s_barrier" ::: "memory"); }
 
-// Grouped MXFP8 x MXFP4 GEMM on the scaled MFMA, for groups with many rows (prefill).
-// Block: 4 WPS waves on one group (expert) and 4 consecutive panels, WPS waves per SIMD. Wave
-// (pm, h) computes panel panel0 + pm on the row tiles h, h + WPS, ... of a chunk of up to ROWS of
-// the group's rows (4 column tiles of 16x16 per row tile, fp32 accumulators); with two waves per
-// SIMD one wave's MFMAs run while the other waits on LDS or on its DMA issues. Per K window of
-// 128, by LDS-DMA (buffer_load ... lds) issued from asm:
-//   - the chunk's activation rows (E4M3 codes, E8M0 scales) into an A stage shared by all waves,
-//     DA windows ahead (16-byte chunk c of row r stored at position c ^ (r & 7));
+// Row-tiled GEMM for many rows per weight set (prefill): MXFP4 weights against MXFP8 activations on
+// the scaled MFMA (grouped: the experts' dispatched rows) or bf16 activations on the bf16 MFMA with
+// the weights converted to bf16 once per window (dense: x and the latent/shared rows, in chunks of
+// ROWS rows that play the part of groups).
+// Block: 4 WPS waves on one group and 4 consecutive panels, WPS waves per SIMD. Wave (pm, h)
+// computes panel panel0 + pm on the row tiles h, h + WPS, ... of a chunk of up to ROWS of the
+// group's rows (4 column tiles of 16x16 per row tile, fp32 accumulators); with two waves per SIMD
+// one wave's MFMAs run while the other waits on LDS or on its DMA issues. Per K window of 128, by
+// LDS-DMA (buffer_load ... lds) issued from asm:
+//   - the chunk's activation rows (MXFP8: E4M3 codes and E8M0 scales) into an A stage shared by all
+//     waves, DA windows ahead (16-byte chunk c of row r stored at position c ^ (r & 7));
 //   - each panel-window of weights into a B stage, DB windows ahead, non-temporal (the weights
-//     come from HBM, the activation rows mostly from L2, hence the deeper weight ring).
+//     come from HBM, the activation rows mostly from L2).
 // Nothing in the loop is a compiler-visible global load: one explicit vmcnt wait and a barrier per
 // window order the DMAs, and the operands are plain LDS reads that the compiler places straight
-// into the MFMA operand registers. One v_mfma_scale_f32_16x16x128_f8f6f4 per (row tile with rows,
-// column tile).
+// into the MFMA operand registers.
 // Blocks are dealt to the XCDs so that every panel block of a group runs on the XCD of that group
 // (group g on XCD g mod 8): the group's activation rows are fetched into one L2 and re-read there.
 // EPI 0: fp32 out. EPI 1: GLU panels, SiLU(gate) * up MX-encoded (E4M3, E8M0 per 32 units),
-// staged in LDS and written as 16-byte row segments.
-template <int DA, int DB, int MT, int WPS, int EPI, int TAG>
-__global__ __launch_bounds__(256 * WPS) void grouped_f8_kernel(GemmArgs args) {
+// staged in LDS and written as 16-byte row segments. EPI 2: the per-panel segment epilogues.
+template <int AF, bool DENSE, int DA, int DB, int MT, int WPS, int EPI, int TAG>
+__global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
+  constexpr bool MX = AF == A_MXFP8;
   constexpr int NWAVE = 4 * WPS;                // WPS waves per SIMD
   constexpr int ROWS = 16 * MT, NA = DA + 1, NB = DB + 1;
   constexpr int MTW = MT / WPS;                 // row tiles per wave
-  constexpr int A_SC = ROWS * 128;
-  constexpr int A_STAGE = A_SC + NWAVE * 256;   // one 256-byte scale slot per wave (64 rows)
+  constexpr int AROW = MX ? 128 : 256;          // bytes of a row's K window
+  constexpr int CPR = AROW / 16;                // 16-byte chunks per row
+  constexpr int RPD = 1024 / AROW;              // rows per 1 KB code DMA
+  constexpr int ESZ = MX ? 1 : 2;               // bytes per activation element
+  constexpr int A_SC = ROWS * AROW;
+  constexpr int A_STAGE = A_SC + (MX ? NWAVE * 256 : 0);  // MXFP8: one 256-byte scale slot per wave
   constexpr int B_STAGE = 4 * kPanelWinBytes;   // one panel-window per panel
-  constexpr int APW = ROWS / 8 / NWAVE;         // 1 KB code DMAs per wave and window (8 rows each)
-  constexpr int AL = APW + 1;                   // + the wave's scale DMA
+  constexpr int APW = ROWS / RPD / NWAVE;       // 1 KB code DMAs per wave and window
+  constexpr int AL = APW + (MX ? 1 : 0);        // + the wave's scale DMA
   constexpr int BPW = (5 + WPS - 1) / WPS;      // a panel's five weight DMAs over its WPS waves
   constexpr int LPW = AL + BPW;
-  static_assert(MT % WPS == 0 && (ROWS / 8) % NWAVE == 0 && ROWS <= 64 * NWAVE, "shape");
+  static_assert(MT % WPS == 0 && (ROWS / RPD) % NWAVE == 0 && (!MX || ROWS <= 64 * NWAVE), "shape");
   static_assert(DB >= DA && DA >= 1, "ring depths");
-  // at step w, A(w) is followed by the B DMAs of the same step and DA - 1 full steps
-  constexpr int WAITN = BPW + (DA - 1) * LPW;
+  // At step w the later of A(w) and B(w) must have landed. DB > DA: A(w) is the later one, followed
+  // by the B DMAs of its step and DA - 1 full steps; DB == DA: B(w) comes last in its step,
+  // followed by DA - 1 full steps.
+  constexpr int WAITN = (DB > DA ? BPW : 0) + (DA - 1) * LPW;
   static_assert(WAITN < 64, "vmcnt range");
-  static_assert(EPI == 0 || ROWS * 132 <= A_STAGE, "epilogue staging fits one A stage");
+  static_assert(EPI != 1 || (MX && ROWS * 132 <= A_STAGE), "epilogue staging fits one A stage");
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[NA][A_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[NB][B_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t lds_sink[NWAVE][256];
@@ -629,44 +639,49 @@ __global__ __launch_bounds__(256 * WPS) void grouped_f8_kernel(GemmArgs args) {
   const int pm = wv & 3, h = wv >> 2;           // panel of the wave, its row-tile phase
   const int nblk = (args.P + 3) / 4;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  // a group: an expert's rows (grouped) or a chunk of ROWS rows (dense, all on the same weights)
   const int grp = xcd + 8 * (slot / nblk);
-  if (grp >= args.n_groups) return;
+  const int ngrp = DENSE ? (args.M + ROWS - 1) / ROWS : args.n_groups;
+  if (grp >= ngrp) return;
   const int panel0 = 4 * (slot % nblk);
-  const int r0 = args.offsets[grp], r1 = args.offsets[grp + 1];
+  const int r0 = DENSE ? grp * ROWS : args.offsets[grp];
+  const int r1 = DENSE ? min(r0 + ROWS, args.M) : args.offsets[grp + 1];
   if (r0 >= r1) return;  // uniform over the block
   const int npan = min(4, args.P - panel0);
   const bool pok = pm < npan;
   const int nwin = args.wwin;
-  const i32x4s wr = sgpr_rsrc(args.W + (int64_t)grp * args.w_group_stride +
+  const i32x4s wr = sgpr_rsrc(args.W + (DENSE ? 0 : (int64_t)grp * args.w_group_stride) +
                                   (int64_t)(pok ? panel0 + pm : 0) * nwin * kPanelWinBytes,
                               pok ? (int64_t)nwin * kPanelWinBytes : 0);
   const i32x4s ar = sgpr_rsrc(args.A, args.a_bytes);
-  const i32x4s asr = sgpr_rsrc(args.A_scales, args.as_bytes);
+  const i32x4s asr = sgpr_rsrc(args.A_scales, MX ? args.as_bytes : 0);
   const int g = lane >> 4, i16 = lane & 15;
   const u32 lds_a0 = lds_addr(&lds_a[0][0]), lds_b0 = lds_addr(&lds_b[0][0]);
   const u32 lds_s = lds_addr(&lds_sink[wv][0]);
 
   for (int mb = r0; mb < r1; mb += ROWS) {
-    // A DMAs of this wave: code instruction j = wv APW + jj covers chunk rows 8 j .. 8 j + 7
-    // (lane L: row 8 j + L / 8, position L % 8 holding chunk (L % 8) ^ (row & 7)); the scale
-    // instruction covers rows 64 wv .. 64 wv + 63 (lane L: row 64 wv + L), zeros past the chunk.
-    int acode[APW], ascale;
+    // A DMAs of this wave: code instruction j = wv APW + jj covers chunk rows RPD j .. RPD j + RPD - 1
+    // (lane L: row RPD j + L / CPR, position L % CPR holding 16-byte chunk (L % CPR) ^ (row & 7) of
+    // the row's window); MXFP8: the scale instruction covers rows 64 wv .. 64 wv + 63 (lane L: row
+    // 64 wv + L). Rows past the chunk and elements past K read zeros.
+    int acode[APW], ascale = -1, akel[APW];
 #pragma unroll
     for (int jj = 0; jj < APW; ++jj) {
-      const int row = mb + 8 * (wv * APW + jj) + (lane >> 3);
+      const int row = mb + RPD * (wv * APW + jj) + lane / CPR;
       acode[jj] = args.rowmap ? args.rowmap[min(row, r1 - 1)] : row;
     }
-    {
+    if constexpr (MX) {
       const int row = mb + 64 * wv + lane;
       ascale = args.rowmap ? args.rowmap[min(row, r1 - 1)] : row;
     }
 #pragma unroll
     for (int jj = 0; jj < APW; ++jj) {
-      const int r = 8 * (wv * APW + jj) + (lane >> 3);
-      const int c = (lane & 7) ^ (r & 7);
-      acode[jj] = mb + r < r1 ? acode[jj] * (int)args.lda + 16 * c : -1;
+      const int r = RPD * (wv * APW + jj) + lane / CPR;
+      const int c = (lane % CPR) ^ (r & 7);
+      akel[jj] = 16 * c / ESZ;  // first K element of the chunk inside the window
+      acode[jj] = mb + r < r1 ? acode[jj] * (int)args.lda * ESZ + 16 * c : -1;
     }
-    ascale = 64 * wv + lane < ROWS && mb + 64 * wv + lane < r1 ? ascale * (int)args.ldas : -1;
+    if constexpr (MX) ascale = 64 * wv + lane < ROWS && mb + 64 * wv + lane < r1 ? ascale * (int)args.ldas : -1;
     const u32 a_w = lds_a0 + 1024 * (wv * APW), a_s = lds_a0 + A_SC + 256 * wv;
     const u32 b_w = lds_b0 + pm * kPanelWinBytes;
     // The LPW DMAs of step w, one by one: the wave's A code DMAs, its A scale DMA, then its share
@@ -681,7 +696,8 @@ __global__ __launch_bounds__(256 * WPS) void grouped_f8_kernel(GemmArgs args) {
         const bool in = real && wa < nwin;
         const u32 st = (u32)((wa % NA) * A_STAGE);
         if constexpr (d < APW)
-          dma16<false>(ar, real ? a_w + st + 1024 * d : lds_s, in && acode[d] >= 0 ? acode[d] + 128 * wa : kOOB);
+          dma16<false>(ar, real ? a_w + st + 1024 * d : lds_s,
+                       in && acode[d] >= 0 && kWinK * wa + akel[d] < args.K ? acode[d] + AROW * wa : kOOB);
         else
           dma4<false>(asr, real ? a_s + st : lds_s, in && ascale >= 0 ? ascale + 4 * wa : kOOB);
       } else {
@@ -726,42 +742,73 @@ __global__ __launch_bounds__(256 * WPS) void grouped_f8_kernel(GemmArgs args) {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) bw[rt] = *(const u32x4*)(sb + rt * 1024 + lane * 16);
         const u32 bsc = *(const u32*)(sb + 4096 + lane * 4);
-        // A operands: row tile t of the stage has its codes at t * 2048 and scales at A_SC + t * 64;
-        // the swizzle depends on the row only through row % 8 = i16 % 8
+        // A operands: row tile t of the stage starts at t * 16 AROW (MXFP8 scales at A_SC + t * 64);
+        // the swizzle depends on the row only through row % 8 = i16 % 8. MXFP8 lane (i16, g): K bytes
+        // [16 g, +16) and [64 + 16 g, +16); bf16 lane (i16, g), step s: K elements [32 g + 8 s, +8).
         const uint8_t* sa = lds_a[w % NA];
-        const uint8_t* plo = sa + i16 * 128 + 16 * (g ^ (i16 & 7)) + h * 2048;
-        const uint8_t* phi = sa + i16 * 128 + 16 * ((4 + g) ^ (i16 & 7)) + h * 2048;
+        const uint8_t* prow = sa + i16 * AROW + h * 16 * AROW;
         const uint8_t* psc = sa + A_SC + i16 * 4 + g + h * 64;
-        auto load_tile = [&](int j, i32x8& aop, int& asc) {  // the wave's j-th tile: row tile h + WPS j
-          const u32x4 lo = *(const u32x4*)(plo + j * WPS * 2048);
-          const u32x4 hi = *(const u32x4*)(phi + j * WPS * 2048);
-          asc = psc[j * WPS * 64];
-          aop = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        using ATileT = std::conditional_t<MX, i32x8, u32x4[4]>;
+        auto load_tile = [&](int j, ATileT& aop, int& asc) {  // the wave's j-th tile: row tile h + WPS j
+          const uint8_t* pr = prow + j * WPS * 16 * AROW;
+          if constexpr (MX) {
+            const u32x4 lo = *(const u32x4*)(pr + 16 * (g ^ (i16 & 7)));
+            const u32x4 hi = *(const u32x4*)(pr + 16 * ((4 + g) ^ (i16 & 7)));
+            asc = psc[j * WPS * 64];
+            aop = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          } else {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) aop[st] = *(const u32x4*)(pr + 16 * ((4 * g + st) ^ (i16 & 7)));
+            asc = 0;
+          }
         };
+        // bf16: the weights as bf16 MFMA operands, converted once per window
+        [[maybe_unused]] bf16x8 bcv[MX ? 1 : 4][MX ? 1 : 4];
+        if constexpr (!MX) {
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int st = 0; st < 4; ++st) bcv[ct][st] = fp4_operand(bw[ct][st], e8m0_f32((bsc >> (8 * ct)) & 0xFFu));
+        }
         // the step's DMAs are spread over the tiles (the wave keeps the matrix core busy while the
         // memory pipeline drains); the next tile's operands are read before each group of DMAs,
         // which are compiler barriers for memory operations
         if constexpr (N == 0) {
           issue_range.template operator()<0, LPW>(w);
         } else {
-          i32x8 cur;
+          ATileT cur;
           int csc;
           load_tile(0, cur, csc);
           [&]<int... JI>(std::integer_sequence<int, JI...>) {
             ([&] {
               constexpr int j = JI;
-              i32x8 nxt;
+              ATileT nxt;
               int nsc = 0;
               if constexpr (j + 1 < N) load_tile(j + 1, nxt, nsc);
+              if constexpr (MX) {
 #pragma unroll
-              for (int ct = 0; ct < 4; ++ct) {
-                const i32x8 bop = {(int)bw[ct][0], (int)bw[ct][1], (int)bw[ct][2], (int)bw[ct][3], 0, 0, 0, 0};
-                acc[j][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur, bop, acc[j][ct], 0, 4, 0, csc, 0,
-                                                                             (int)(bsc >> (8 * ct)));
+                for (int ct = 0; ct < 4; ++ct) {
+                  const i32x8 bop = {(int)bw[ct][0], (int)bw[ct][1], (int)bw[ct][2], (int)bw[ct][3], 0, 0, 0, 0};
+                  acc[j][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur, bop, acc[j][ct], 0, 4, 0, csc,
+                                                                               0, (int)(bsc >> (8 * ct)));
+                }
+              } else {
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                  const bf16x8 av = __builtin_bit_cast(bf16x8, cur[st]);
+#pragma unroll
+                  for (int ct = 0; ct < 4; ++ct)
+                    acc[j][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bcv[ct][st], acc[j][ct], 0, 0, 0);
+                }
               }
               issue_range.template operator()<j * LPW / N, (j + 1) * LPW / N>(w);
               if constexpr (j + 1 < N) {
-                cur = nxt;
+                if constexpr (MX) {
+                  cur = nxt;
+                } else {
+#pragma unroll
+                  for (int st = 0; st < 4; ++st) cur[st] = nxt[st];
+                }
                 csc = nsc;
               }
             }(), ...);
@@ -826,6 +873,13 @@ __global__ __launch_bounds__(256 * WPS) void grouped_f8_kernel(GemmArgs args) {
         else
           for (int p = 0; p < npan; ++p) os[p] = stg_sc[4 * lr + p];
       }
+    } else if constexpr (EPI == 2) {
+      // per-panel segment modes (sigmoid, bf16, MX encode, SwiGLU, bf16 + addend)
+      if (pok) {
+#pragma unroll
+        for (int j = 0; j < MTW; ++j)
+          if (16 * (h + WPS * j) < nrow) epilogue(args, acc[j], panel0 + pm, mb + 16 * (h + WPS * j), r1, ln);
+      }
     } else {
       const rsrc_t orr = make_rsrc((float*)sg.out + (int64_t)mb * sg.ldo + sg.col0, (int64_t)nrow * sg.ldo * 4);
 #pragma unroll
@@ -847,6 +901,7 @@ __global__ __launch_bounds__(256 * WPS) void grouped_f8_kernel(GemmArgs args) {
   }
 }
 
+
 template <int KSPLIT, int AFMT, int NBUF, int MT, bool AHEAD, int TAG>
 static void launch_one(GemmArgs a, hipStream_t s) {
   constexpr int ppb = BlockShape<KSPLIT>::panels;
@@ -862,7 +917,7 @@ static void launch_one(GemmArgs a, hipStream_t s) {
                      0, s, a);
 }
 
-// The scaled-MFMA grouped kernel takes grouped launches with many rows per group, whole K windows,
+// The row-tiled kernel takes grouped MXFP8 launches with many rows per group, whole K windows,
 // 16-byte aligned activation rows, 4-byte aligned scale rows and one epilogue segment of the given
 // mode (GLU output rows 16-byte aligned, scale rows 4-byte aligned at panel-block granularity).
 static bool f8_grouped_ok(const GemmArgs& a, int mode) {
@@ -879,7 +934,24 @@ static void launch_f8(const GemmArgs& a, hipStream_t s) {
   constexpr int DA = 2, DB = 3, MT = 12, WPS = 2;
   const unsigned nblk = (unsigned)ceil_div(a.P, 4);
   const unsigned g8 = (unsigned)ceil_div(a.n_groups, 8) * 8;
-  hipLaunchKernelGGL((grouped_f8_kernel<DA, DB, MT, WPS, EPI, TAG>), dim3(g8 * nblk), dim3(256 * WPS), 0, s, a);
+  hipLaunchKernelGGL((tiled_gemm_kernel<A_MXFP8, false, DA, DB, MT, WPS, EPI, TAG>), dim3(g8 * nblk), dim3(256 * WPS),
+                     0, s, a);
+}
+
+// Dense bf16 launches with enough rows to fill the chip with 128-row chunks (8 per XCD) take the
+// row-tiled kernel; rows must be 16-byte aligned.
+constexpr int kDenseRows = 128;
+static bool dense_tiled_ok(const GemmArgs& a) {
+  return !a.offsets && a.a_fmt == A_BF16 && a.M >= 8 * kDenseRows && a.lda % 8 == 0 && a.K % 32 == 0;
+}
+
+template <int TAG>
+static void launch_dense_tiled(const GemmArgs& a, hipStream_t s) {
+  constexpr int DA = 2, DB = 2, MT = kDenseRows / 16, WPS = 2;
+  const unsigned nblk = (unsigned)ceil_div(a.P, 4);
+  const unsigned g8 = (unsigned)ceil_div(ceil_div(a.M, kDenseRows), 8) * 8;
+  hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, true, DA, DB, MT, WPS, 2, TAG>), dim3(g8 * nblk), dim3(256 * WPS), 0,
+                     s, a);
 }
 
 hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) {
@@ -887,10 +959,16 @@ hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) 
   if (a.offsets == nullptr && a.M <= 0) return hipSuccess;
   switch (stage) {
     case GEMM_X:
-      launch_one<8, A_BF16, 3, 1, true, GEMM_X>(a, s);
+      if (dense_tiled_ok(a))
+        launch_dense_tiled<GEMM_X>(a, s);
+      else
+        launch_one<8, A_BF16, 3, 1, true, GEMM_X>(a, s);
       break;
     case GEMM_Y:
-      launch_one<8, A_BF16, 3, 1, true, GEMM_Y>(a, s);
+      if (dense_tiled_ok(a))
+        launch_dense_tiled<GEMM_Y>(a, s);
+      else
+        launch_one<8, A_BF16, 3, 1, true, GEMM_Y>(a, s);
       break;
     case GEMM_GATEUP:
       if (a.a_fmt == A_BF16)

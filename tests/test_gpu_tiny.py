@@ -130,8 +130,8 @@ def check_all(name, T):
     return g
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_mxfp8", "tiny_mxfp8_many", "tiny_mxfp8_deep", "tiny_fullwidth",
-                                  "tiny_skewed"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_mxfp8", "tiny_mxfp8_many", "tiny_mxfp8_deep", "tiny_dense_many",
+                                  "tiny_fullwidth", "tiny_skewed"])
 def test_full_parity(name):
     check_all(name, workloads.get(name).T)
 
@@ -155,6 +155,12 @@ def test_mxfp8_many_rows_ragged(T):
 def test_mxfp8_deep_ragged(T):
     """Scaled-MFMA grouped kernel over several K windows and several 256-row chunks per expert."""
     check_all("tiny_mxfp8_deep", T)
+
+
+@pytest.mark.parametrize("T", [1024, 1500])
+def test_dense_many_rows_ragged(T):
+    """Row-tiled dense GEMMs: 128-row chunks with a partial last chunk."""
+    check_all("tiny_dense_many", T)
 
 
 def test_deterministic_and_stream_order():

@@ -205,6 +205,9 @@ WORKLOADS = {
                                 zipf_alpha=0.2,
                                 note="tiny layer, MXFP8, several K windows, skewed rows per expert (some above "
                                      "256: several row chunks)"),
+    "tiny_dense_many": Workload("tiny_dense_many", LayerShape(d=256, l=128, h=96, E=16, k=4, Ns=1, hs=96), T=2048,
+                                seed=8, note="tiny layer, bf16, 2048 tokens (row-tiled dense GEMMs, K tail "
+                                             "in the latent/shared GEMM)"),
     "tiny_fullwidth": Workload("tiny_fullwidth", LayerShape(d=256, l=256, h=96, E=16, k=2, Ns=1, hs=96,
                                                             latent_moe=0), T=64, seed=5,
                                note="tiny conventional full-width MoE"),
