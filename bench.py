@@ -7,9 +7,11 @@ bf16 activations; seeded synthetic inputs (x ~ N(0, 1), weights ~ N(0, 1/fan_in)
 MXFP4). A step is one full layer forward (x_gemm, topk, route, gateup, down, combine, y_gemm)
 with inputs resident in HBM.
 
-Prints one JSON line: tokens/s, the roofline of the dominant kernel (the grouped gate/up GEMM,
-HBM-bound at decode) from per-stage HIP events recorded on the launch stream over the timed
-region, and the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (the grouped gate/up GEMM:
+HBM-bound at decode, MFMA-bound at prefill with MXFP8 activations) from per-stage HIP events
+recorded on the launch stream over the timed region, the layer's HBM rate and MFMA fraction
+(its time at the peaks of the dtypes each stage computes in, over the measured time), and the
+CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -23,7 +25,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published (the scaled MFMA with an fp8 operand)
+MXFP4_PEAK_TFLOPS = 10100.0    # MI355X dense MXFP4 (fp4 x fp4) scaled MFMA, published
 
 
 def log(msg):
@@ -125,8 +129,27 @@ def main():
     gu_alg = n_active * gu_bytes_expert + rows * le * act_b + rows * s.h * act_b
     layer_alg = n_active * (gu_bytes_expert + dn_bytes_expert) + dense_bytes + 2 * T * s.d * 2
     gu_ms = stage_avg["gateup"]
-    achieved = gu_alg / (gu_ms * 1e-3) / 1e9
     flops_tok = 2 * (s.E * s.d + (2 * s.d * s.l if s.latent_moe else 0) + s.k * 3 * le * s.h + s.Ns * 3 * s.d * s.hs)
+    # MFMA work per stage and the layer's time at the peaks of the dtypes the stages compute in
+    dense_flops = 2 * T * (s.E * s.d + (2 * s.d * s.l if s.latent_moe else 0) + s.Ns * 3 * s.d * s.hs)
+    routed_flops = 2 * rows * 3 * le * s.h
+    routed_peak = FP8_PEAK_TFLOPS if s.act == "mxfp8" else BF16_PEAK_TFLOPS
+    ideal_ms = (dense_flops / BF16_PEAK_TFLOPS + routed_flops / routed_peak) / 1e9
+    gu_flops = 2 * rows * 2 * s.h * le
+    traffic = recorded_traffic(wl.name, "gateup")
+    if s.act == "mxfp8":
+        # prefill: the grouped gate/up GEMM is MFMA-bound (MXFP8 x MXFP4 scaled MFMA at the fp8 rate)
+        achieved = gu_flops / (gu_ms * 1e-3) / 1e12
+        roofline = {"kernel": "gateup (grouped GLU gate/up GEMM, MXFP8 x MXFP4 scaled MFMA)", "bound": "mfma",
+                    "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / FP8_PEAK_TFLOPS,
+                    "traffic": traffic, "algorithmic_flops_per_launch": gu_flops,
+                    "algorithmic_bytes_per_launch": gu_alg, "avg_launch_ms": gu_ms,
+                    "frac_of_mxfp4_peak": achieved / MXFP4_PEAK_TFLOPS}
+    else:
+        achieved = gu_alg / (gu_ms * 1e-3) / 1e9
+        roofline = {"kernel": "gateup (grouped GLU gate/up GEMM, MXFP4 weight stream)", "bound": "hbm",
+                    "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                    "traffic": traffic, "algorithmic_bytes_per_launch": gu_alg, "avg_launch_ms": gu_ms}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -143,18 +166,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8 x mxfp4" if s.act == "mxfp8" else "bf16 x mxfp4",
         "data": "synthetic (seeded: x ~ N(0,1) bf16; weights ~ N(0,1/fan_in) quantised to MXFP4)",
         "config": {"workload": wl.name, "tokens": T, "d": s.d, "latent": s.l if s.latent_moe else None,
                    "hidden": s.h, "experts": s.E, "top_k": s.k, "shared": s.Ns, "act": s.act,
                    "latent_moe": s.latent_moe, "weights": "MXFP4", "parallelism": "single GPU"},
-        "roofline": {"kernel": "gateup (grouped GLU gate/up GEMM, MXFP4 weight stream)", "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": recorded_traffic(wl.name, "gateup"), "algorithmic_bytes_per_launch": gu_alg,
-                     "avg_launch_ms": gu_ms},
+        "roofline": roofline,
         "layer_hbm_gbps": layer_alg / (ms_step * 1e-3) / 1e9,
+        "layer_hbm_frac": layer_alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "layer_algorithmic_bytes": layer_alg,
         "layer_tflops": flops_tok * T / (ms_step * 1e-3) / 1e12,
+        "layer_mfma_frac": ideal_ms / ms_step,
         "active_experts": n_active,
         "max_over_mean_load": float(counts.max() / max(counts.mean(), 1e-9)),
         "stages_ms": stage_avg,
