@@ -46,7 +46,7 @@ struct k3moe_ctx {
   size_t off_x = 0, off_y = 0, off_gu = 0, off_dn = 0, off_bias = 0, off_gamma = 0, total = 0;
   size_t gu_stride = 0, dn_stride = 0;
   // workspace layout (for max_tokens)
-  size_t ws_scores = 0, ws_idx = 0, ws_p = 0, ws_counts = 0, ws_offsets = 0, ws_perm = 0, ws_inv = 0;
+  size_t ws_scores = 0, ws_idx = 0, ws_p = 0, ws_counts = 0, ws_offsets = 0, ws_perm = 0, ws_inv = 0, ws_route = 0;
   size_t ws_z = 0, ws_zs = 0, ws_h = 0, ws_hs = 0, ws_o = 0, ws_abuf = 0, ws_u = 0, ws_total = 0;
   // state
   uint8_t* packed = nullptr;
@@ -173,6 +173,7 @@ int k3moe_create(const k3moe_config* cfg, k3moe_ctx** out) {
   x->ws_offsets = take(4 * ((size_t)E + 1));
   x->ws_perm = take(4 * T * k);
   x->ws_inv = take(4 * T * k);
+  x->ws_route = take((size_t)route_scratch_bytes(c.max_tokens, c.n_experts));
   const bool f8 = c.act == K3MOE_ACT_MXFP8;
   if (c.latent_moe) {
     x->ws_z = take((f8 ? 1 : 2) * T * l);
@@ -456,7 +457,8 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
   HIPCHECK(ctx, mark(ST_TOPK, 1), "event");
   // ---- route
   HIPCHECK(ctx, mark(ST_ROUTE, 0), "event");
-  HIPCHECK(ctx, launch_route(idx, T, E, k, counts, offsets, perm, inv, s), "route launch");
+  HIPCHECK(ctx, launch_route(idx, T, E, k, counts, offsets, perm, inv, (int32_t*)(ws + ctx->ws_route), s),
+           "route launch");
   HIPCHECK(ctx, mark(ST_ROUTE, 1), "event");
   // Experts averaging 32 or more rows use the LDS-tiled scaled-MFMA kernel (MXFP8 activations;
   // its DMAs move whole 4-byte scale words, so both reduction widths must be multiples of 128)

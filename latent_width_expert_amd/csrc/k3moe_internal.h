@@ -108,8 +108,11 @@ hipError_t launch_pack(const PackJob& job, hipStream_t s);
 hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s);
 hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* idx, float* p,
                        hipStream_t s);
+// scratch: route_scratch_bytes(max_tokens, E) bytes of workspace (per-chunk expert counts); small T
+// (or scratch == null) takes the single-block kernel
 hipError_t launch_route(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
-                        int32_t* inv, hipStream_t s);
+                        int32_t* inv, int32_t* scratch, hipStream_t s);
+int64_t route_scratch_bytes(int max_tokens, int E);
 // mode 0: n = bf16(gamma * u / sqrt(mean(u^2) + eps)) into n_out (ld ldn); mode 1: u only
 hipError_t launch_combine(const float* O, const int32_t* inv, const float* p, int T, int k, int width,
                           const float* gamma, float eps, int mode, uint16_t* n_out, int64_t ldn, float* u_out,

@@ -1154,10 +1154,109 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t* __r
   }
 }
 
+// The same tables for many tokens, in parallel over 64-token chunks (same result):
+//   route_chunk:   per chunk, each entry's rank among the chunk's entries of its expert (64-bit
+//                  LDS masks as above) and the chunk's count per expert;
+//   route_scan:    per expert (one wave), the exclusive scan of its chunk counts over the chunks
+//                  (the expert's rows before the chunk) and its total;
+//   route_offsets: the exclusive scan of the totals over the experts;
+//   route_scatter: row = offsets[e] + rows of e before the chunk + rank in the chunk.
+constexpr int kRouteChunk = 64;
+
+__global__ __launch_bounds__(256) void route_chunk_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+                                                          int32_t* __restrict__ rank, int32_t* __restrict__ ccount) {
+  __shared__ unsigned long long mask[kMaxExperts];
+  const int c = blockIdx.x, tid = threadIdx.x;
+  const int t0 = c * kRouteChunk, ntok = min(kRouteChunk, T - t0);
+  for (int e = tid; e < E; e += 256) mask[e] = 0ull;
+  __syncthreads();
+  for (int q = tid; q < ntok * k; q += 256) {
+    const int e = min(max(idx[(int64_t)t0 * k + q], 0), E - 1);
+    atomicOr(&mask[e], 1ull << (q / k));
+  }
+  __syncthreads();
+  for (int q = tid; q < ntok * k; q += 256) {
+    const int e = min(max(idx[(int64_t)t0 * k + q], 0), E - 1);
+    const int tl = q / k;
+    rank[(int64_t)t0 * k + q] = tl ? __popcll(mask[e] & ((1ull << tl) - 1ull)) : 0;
+  }
+  for (int e = tid; e < E; e += 256) ccount[(int64_t)c * E + e] = __popcll(mask[e]);
+}
+
+__global__ __launch_bounds__(256) void route_scan_kernel(int nchunk, int E, int32_t* __restrict__ ccount,
+                                                         int32_t* __restrict__ counts) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (e >= E) return;  // uniform per wave
+  int carry = 0;
+  for (int c0 = 0; c0 < nchunk; c0 += 64) {
+    const int c = c0 + lane;
+    const int v = c < nchunk ? ccount[(int64_t)c * E + e] : 0;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+    if (c < nchunk) ccount[(int64_t)c * E + e] = carry + incl - v;  // rows of e before chunk c
+    carry += __shfl(incl, 63);
+  }
+  if (lane == 0) counts[e] = carry;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_offsets_kernel(int E, const int32_t* __restrict__ counts,
+                                                                      int32_t* __restrict__ offsets) {
+  __shared__ int32_t part[kRouteThreads];
+  const int tid = threadIdx.x;
+  const int per = (E + kRouteThreads - 1) / kRouteThreads;
+  const int e0 = tid * per, e1 = min(E, e0 + per);
+  int run = 0;
+  for (int e = e0; e < e1; ++e) run += counts[e];
+  part[tid] = run;
+  __syncthreads();
+  for (int off = 1; off < kRouteThreads; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int acc = part[tid] - run;
+  for (int e = e0; e < e1; ++e) {
+    offsets[e] = acc;
+    acc += counts[e];
+  }
+  if (tid == kRouteThreads - 1) offsets[E] = part[kRouteThreads - 1];
+}
+
+__global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* __restrict__ idx, int T, int E, int k,
+                                                            const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ cbase, int32_t* __restrict__ inv,
+                                                            int32_t* __restrict__ perm) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= (int64_t)T * k) return;
+  const int e = min(max(idx[q], 0), E - 1);
+  const int t = (int)(q / k);
+  const int row = offsets[e] + cbase[(int64_t)(t / kRouteChunk) * E + e] + inv[q];
+  inv[q] = row;
+  perm[row] = t;
+}
+
+int64_t route_scratch_bytes(int max_tokens, int E) {
+  return (int64_t)ceil_div(max_tokens, kRouteChunk) * E * 4;
+}
+
 hipError_t launch_route(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
-                        int32_t* inv, hipStream_t s) {
-  if (E > kMaxExperts) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, idx, T, E, k, counts, offsets, perm, inv);
+                        int32_t* inv, int32_t* scratch, hipStream_t s) {
+  if (E > kMaxExperts || k > kRouteChunk) return hipErrorInvalidValue;
+  if (T <= 8 * kRouteChunk || scratch == nullptr) {
+    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, idx, T, E, k, counts, offsets, perm, inv);
+    return hipGetLastError();
+  }
+  const int nchunk = (int)ceil_div(T, kRouteChunk);
+  hipLaunchKernelGGL(route_chunk_kernel, dim3(nchunk), dim3(256), 0, s, idx, T, E, k, inv, scratch);
+  hipLaunchKernelGGL(route_scan_kernel, dim3((unsigned)ceil_div(E, 4)), dim3(256), 0, s, nchunk, E, scratch, counts);
+  hipLaunchKernelGGL(route_offsets_kernel, dim3(1), dim3(kRouteThreads), 0, s, E, (const int32_t*)counts, offsets);
+  hipLaunchKernelGGL(route_scatter_kernel, dim3((unsigned)ceil_div((int64_t)T * k, 256)), dim3(256), 0, s, idx, T, E,
+                     k, (const int32_t*)offsets, (const int32_t*)scratch, inv, perm);
   return hipGetLastError();
 }
 
