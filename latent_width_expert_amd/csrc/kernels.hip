@@ -605,12 +605,14 @@ __device__ __forceinline__ void barrier_nowait() { asm volatile("s_barrier" ::: 
 // (group g on XCD g mod 8): the group's activation rows are fetched into one L2 and re-read there.
 // EPI 0: fp32 out. EPI 1: GLU panels, SiLU(gate) * up MX-encoded (E4M3, E8M0 per 32 units),
 // staged in LDS and written as 16-byte row segments. EPI 2: the per-panel segment epilogues.
-template <int AF, bool DENSE, int DA, int DB, int MT, int WPS, int EPI, int TAG>
+template <int AF, bool DENSE, int DA, int DB, int MT, int WPS, int PPW, int EPI, int TAG>
 __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
   constexpr bool MX = AF == A_MXFP8;
   constexpr int NWAVE = 4 * WPS;                // WPS waves per SIMD
   constexpr int ROWS = 16 * MT, NA = DA + 1, NB = DB + 1;
-  constexpr int MTW = MT / WPS;                 // row tiles per wave
+  constexpr int NPG = 4 / PPW;                  // panel groups (PPW panels each)
+  constexpr int NPH = NWAVE / NPG;              // row-tile phases
+  constexpr int MTW = MT / NPH;                 // row tiles per wave
   constexpr int AROW = MX ? 128 : 256;          // bytes of a row's K window
   constexpr int CPR = AROW / 16;                // 16-byte chunks per row
   constexpr int RPD = 1024 / AROW;              // rows per 1 KB code DMA
@@ -620,9 +622,9 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
   constexpr int B_STAGE = 4 * kPanelWinBytes;   // one panel-window per panel
   constexpr int APW = ROWS / RPD / NWAVE;       // 1 KB code DMAs per wave and window
   constexpr int AL = APW + (MX ? 1 : 0);        // + the wave's scale DMA
-  constexpr int BPW = (5 + WPS - 1) / WPS;      // a panel's five weight DMAs over its WPS waves
+  constexpr int BPW = (20 + NWAVE - 1) / NWAVE; // the four panels' 5 weight DMAs each, over the waves
   constexpr int LPW = AL + BPW;
-  static_assert(MT % WPS == 0 && (ROWS / RPD) % NWAVE == 0 && (!MX || ROWS <= 64 * NWAVE), "shape");
+  static_assert(4 % PPW == 0 && MT % NPH == 0 && (ROWS / RPD) % NWAVE == 0 && (!MX || ROWS <= 64 * NWAVE), "shape");
   static_assert(DB >= DA && DA >= 1, "ring depths");
   // At step w the later of A(w) and B(w) must have landed. DB > DA: A(w) is the later one, followed
   // by the B DMAs of its step and DA - 1 full steps; DB == DA: B(w) comes last in its step,
@@ -636,23 +638,23 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int pm = wv & 3, h = wv >> 2;           // panel of the wave, its row-tile phase
+  const int pg = wv % NPG, h = wv / NPG;        // panel group of the wave, its row-tile phase
   const int nblk = (args.P + 3) / 4;
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   // a group: an expert's rows (grouped) or a chunk of ROWS rows (dense, all on the same weights)
   const int grp = xcd + 8 * (slot / nblk);
+  const int panel0 = 4 * (slot % nblk);
   const int ngrp = DENSE ? (args.M + ROWS - 1) / ROWS : args.n_groups;
   if (grp >= ngrp) return;
-  const int panel0 = 4 * (slot % nblk);
   const int r0 = DENSE ? grp * ROWS : args.offsets[grp];
   const int r1 = DENSE ? min(r0 + ROWS, args.M) : args.offsets[grp + 1];
   if (r0 >= r1) return;  // uniform over the block
   const int npan = min(4, args.P - panel0);
-  const bool pok = pm < npan;
   const int nwin = args.wwin;
+  // the block's (up to) four panels, one resource: panel p's window w at (p nwin + w) 4352
   const i32x4s wr = sgpr_rsrc(args.W + (DENSE ? 0 : (int64_t)grp * args.w_group_stride) +
-                                  (int64_t)(pok ? panel0 + pm : 0) * nwin * kPanelWinBytes,
-                              pok ? (int64_t)nwin * kPanelWinBytes : 0);
+                                  (int64_t)panel0 * nwin * kPanelWinBytes,
+                              (int64_t)npan * nwin * kPanelWinBytes);
   const i32x4s ar = sgpr_rsrc(args.A, args.a_bytes);
   const i32x4s asr = sgpr_rsrc(args.A_scales, MX ? args.as_bytes : 0);
   const int g = lane >> 4, i16 = lane & 15;
@@ -683,11 +685,10 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
     }
     if constexpr (MX) ascale = 64 * wv + lane < ROWS && mb + 64 * wv + lane < r1 ? ascale * (int)args.ldas : -1;
     const u32 a_w = lds_a0 + 1024 * (wv * APW), a_s = lds_a0 + A_SC + 256 * wv;
-    const u32 b_w = lds_b0 + pm * kPanelWinBytes;
     // The LPW DMAs of step w, one by one: the wave's A code DMAs, its A scale DMA, then its share
-    // of the panel's five weight DMAs (items h BPW .. h BPW + BPW - 1 of: four 1 KB code pieces,
-    // the 256-byte scale piece; items past five are 4-byte dummies into the wave's sink), always
-    // in this order so that one wait count holds at every step. Step w fills A stage
+    // of the four panels' weight DMAs (items wv BPW .. wv BPW + BPW - 1 of: per panel four 1 KB code
+    // pieces and the 256-byte scale piece; items past 20 are 4-byte dummies into the wave's sink),
+    // always in this order so that one wait count holds at every step. Step w fills A stage
     // (w + DA) % NA and B stage (w + DB) % NB; a stage index below zero in the prologue is a dummy.
     auto issue_one = [&]<int d>(int w) {
       if constexpr (d < AL) {
@@ -702,15 +703,17 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
           dma4<false>(asr, real ? a_s + st : lds_s, in && ascale >= 0 ? ascale + 4 * wa : kOOB);
       } else {
         const int wb = w + DB;
-        const bool in = wb < nwin;
-        const u32 st = b_w + (u32)((wb % NB) * B_STAGE);
-        const int item = h * BPW + (d - AL);  // uniform
-        if (item < 4)
-          dma16<true>(wr, st + 1024 * item, in ? lane * 16 + wb * kPanelWinBytes + 1024 * item : kOOB);
-        else if (item == 4)
-          dma4<true>(wr, st + 4096, in ? lane * 4 + wb * kPanelWinBytes + 4096 : kOOB);
-        else
+        const int item = wv * BPW + (d - AL);  // uniform
+        const int p = item / 5, piece = item % 5;
+        const bool in = wb < nwin && p < npan;
+        const u32 st = lds_b0 + (u32)((wb % NB) * B_STAGE + p * kPanelWinBytes);
+        const int src = (p * nwin + wb) * kPanelWinBytes;
+        if (item >= 20)
           dma4<false>(wr, lds_s, kOOB);
+        else if (piece < 4)
+          dma16<true>(wr, st + 1024 * piece, in ? src + 1024 * piece + lane * 16 : kOOB);
+        else
+          dma4<true>(wr, st + 4096, in ? src + 4096 + lane * 4 : kOOB);
       }
     };
     auto issue_range = [&]<int D0, int D1>(int w) {
@@ -718,15 +721,17 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
         (issue_one.template operator()<D0 + I>(w), ...);
       }(std::make_integer_sequence<int, D1 - D0>{});
     };
-    // row tiles holding rows (uniform over the block) and this wave's share: tiles h, h + WPS, ...
+    // row tiles holding rows (uniform over the block) and this wave's share: tiles h, h + NPH, ...
     const int nt = min(MT, (r1 - mb + 15) / 16);
-    const int nw = nt > h ? (nt - h + WPS - 1) / WPS : 0;
+    const int nw = nt > h ? (nt - h + NPH - 1) / NPH : 0;
 
-    f32x4 acc[MTW][4];
+    f32x4 acc[MTW][PPW][4];
 #pragma unroll
     for (int j = 0; j < MTW; ++j)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) acc[j][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int pp = 0; pp < PPW; ++pp)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[j][pp][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // The window loop, specialised on the wave's number of row tiles holding rows (one variant per
     // count, chosen once per chunk) so that each window's body is straight-line code.
@@ -736,12 +741,16 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
       for (int w = 0; w < nwin; ++w) {
         wait_vmcnt<WAITN>();
         barrier_nowait();  // stages of w complete for every wave; stages of w - 1 free
-        // weights of the wave's panel-window
-        const uint8_t* sb = &lds_b[w % NB][pm * kPanelWinBytes];
-        u32x4 bw[4];
+        // weights of the wave's panel-windows
+        u32x4 bw[PPW][4];
+        u32 bsc[PPW];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) bw[rt] = *(const u32x4*)(sb + rt * 1024 + lane * 16);
-        const u32 bsc = *(const u32*)(sb + 4096 + lane * 4);
+        for (int pp = 0; pp < PPW; ++pp) {
+          const uint8_t* sb = &lds_b[w % NB][(PPW * pg + pp) * kPanelWinBytes];
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) bw[pp][rt] = *(const u32x4*)(sb + rt * 1024 + lane * 16);
+          bsc[pp] = *(const u32*)(sb + 4096 + lane * 4);
+        }
         // A operands: row tile t of the stage starts at t * 16 AROW (MXFP8 scales at A_SC + t * 64);
         // the swizzle depends on the row only through row % 8 = i16 % 8. MXFP8 lane (i16, g): K bytes
         // [16 g, +16) and [64 + 16 g, +16); bf16 lane (i16, g), step s: K elements [32 g + 8 s, +8).
@@ -749,12 +758,12 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
         const uint8_t* prow = sa + i16 * AROW + h * 16 * AROW;
         const uint8_t* psc = sa + A_SC + i16 * 4 + g + h * 64;
         using ATileT = std::conditional_t<MX, i32x8, u32x4[4]>;
-        auto load_tile = [&](int j, ATileT& aop, int& asc) {  // the wave's j-th tile: row tile h + WPS j
-          const uint8_t* pr = prow + j * WPS * 16 * AROW;
+        auto load_tile = [&](int j, ATileT& aop, int& asc) {  // the wave's j-th tile: row tile h + NPH j
+          const uint8_t* pr = prow + j * NPH * 16 * AROW;
           if constexpr (MX) {
             const u32x4 lo = *(const u32x4*)(pr + 16 * (g ^ (i16 & 7)));
             const u32x4 hi = *(const u32x4*)(pr + 16 * ((4 + g) ^ (i16 & 7)));
-            asc = psc[j * WPS * 64];
+            asc = psc[j * NPH * 64];
             aop = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
           } else {
 #pragma unroll
@@ -763,12 +772,15 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
           }
         };
         // bf16: the weights as bf16 MFMA operands, converted once per window
-        [[maybe_unused]] bf16x8 bcv[MX ? 1 : 4][MX ? 1 : 4];
+        [[maybe_unused]] bf16x8 bcv[MX ? 1 : PPW][MX ? 1 : 4][MX ? 1 : 4];
         if constexpr (!MX) {
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
+          for (int pp = 0; pp < PPW; ++pp)
 #pragma unroll
-            for (int st = 0; st < 4; ++st) bcv[ct][st] = fp4_operand(bw[ct][st], e8m0_f32((bsc >> (8 * ct)) & 0xFFu));
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+              for (int st = 0; st < 4; ++st)
+                bcv[pp][ct][st] = fp4_operand(bw[pp][ct][st], e8m0_f32((bsc[pp] >> (8 * ct)) & 0xFFu));
         }
         // the step's DMAs are spread over the tiles (the wave keeps the matrix core busy while the
         // memory pipeline drains); the next tile's operands are read before each group of DMAs,
@@ -787,18 +799,24 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
               if constexpr (j + 1 < N) load_tile(j + 1, nxt, nsc);
               if constexpr (MX) {
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct) {
-                  const i32x8 bop = {(int)bw[ct][0], (int)bw[ct][1], (int)bw[ct][2], (int)bw[ct][3], 0, 0, 0, 0};
-                  acc[j][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur, bop, acc[j][ct], 0, 4, 0, csc,
-                                                                               0, (int)(bsc >> (8 * ct)));
-                }
+                for (int pp = 0; pp < PPW; ++pp)
+#pragma unroll
+                  for (int ct = 0; ct < 4; ++ct) {
+                    const i32x8 bop = {(int)bw[pp][ct][0], (int)bw[pp][ct][1], (int)bw[pp][ct][2], (int)bw[pp][ct][3],
+                                       0, 0, 0, 0};
+                    acc[j][pp][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        cur, bop, acc[j][pp][ct], 0, 4, 0, csc, 0, (int)(bsc[pp] >> (8 * ct)));
+                  }
               } else {
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
                   const bf16x8 av = __builtin_bit_cast(bf16x8, cur[st]);
 #pragma unroll
-                  for (int ct = 0; ct < 4; ++ct)
-                    acc[j][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bcv[ct][st], acc[j][ct], 0, 0, 0);
+                  for (int pp = 0; pp < PPW; ++pp)
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+                      acc[j][pp][ct] =
+                          __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bcv[pp][ct][st], acc[j][pp][ct], 0, 0, 0);
                 }
               }
               issue_range.template operator()<j * LPW / N, (j + 1) * LPW / N>(w);
@@ -839,21 +857,25 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
 #pragma unroll
       for (int j = 0; j < MTW; ++j) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v0 = silu(acc[j][0][r]) * acc[j][1][r];
-          const float v1 = silu(acc[j][2][r]) * acc[j][3][r];
-          const int lr = 16 * (h + WPS * j) + 4 * eg + r;
-          if (tap) {
-            const int o = lr * (int)sg.ldpre + sg.col0 + 32 * (panel0 + pm) + ej;
-            const bool ok = lr < nrow && pok;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), prr, ok ? 4 * o : kOOB, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), prr, ok ? 4 * (o + 16) : kOOB, 0, 0);
+        for (int pp = 0; pp < PPW; ++pp) {
+          const int pl = PPW * pg + pp;  // panel inside the block
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float v0 = silu(acc[j][pp][0][r]) * acc[j][pp][1][r];
+            const float v1 = silu(acc[j][pp][2][r]) * acc[j][pp][3][r];
+            const int lr = 16 * (h + NPH * j) + 4 * eg + r;
+            if (tap) {
+              const int o = lr * (int)sg.ldpre + sg.col0 + 32 * (panel0 + pl) + ej;
+              const bool ok = lr < nrow && pl < npan;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), prr, ok ? 4 * o : kOOB, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), prr, ok ? 4 * (o + 16) : kOOB, 0, 0);
+            }
+            u32 c0, c1, sb;
+            mxfp8_block(v0, v1, c0, c1, sb);
+            stg[lr * 128 + 32 * pl + ej] = (uint8_t)c0;
+            stg[lr * 128 + 32 * pl + 16 + ej] = (uint8_t)c1;
+            stg_sc[lr * 4 + pl] = (uint8_t)sb;  // the 16 lanes of the block agree
           }
-          u32 c0, c1, sb;
-          mxfp8_block(v0, v1, c0, c1, sb);
-          stg[lr * 128 + 32 * pm + ej] = (uint8_t)c0;
-          stg[lr * 128 + 32 * pm + 16 + ej] = (uint8_t)c1;
-          stg_sc[lr * 4 + pm] = (uint8_t)sb;  // the 16 lanes of the block agree
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -875,24 +897,32 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
       }
     } else if constexpr (EPI == 2) {
       // per-panel segment modes (sigmoid, bf16, MX encode, SwiGLU, bf16 + addend)
-      if (pok) {
 #pragma unroll
-        for (int j = 0; j < MTW; ++j)
-          if (16 * (h + WPS * j) < nrow) epilogue(args, acc[j], panel0 + pm, mb + 16 * (h + WPS * j), r1, ln);
+      for (int pp = 0; pp < PPW; ++pp) {
+        if (PPW * pg + pp < npan) {
+#pragma unroll
+          for (int j = 0; j < MTW; ++j)
+            if (16 * (h + NPH * j) < nrow)
+              epilogue(args, acc[j][pp], panel0 + PPW * pg + pp, mb + 16 * (h + NPH * j), r1, ln);
+        }
       }
     } else {
       const rsrc_t orr = make_rsrc((float*)sg.out + (int64_t)mb * sg.ldo + sg.col0, (int64_t)nrow * sg.ldo * 4);
 #pragma unroll
       for (int j = 0; j < MTW; ++j) {
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const int col = 64 * (panel0 + pm) + 16 * ct + ej;
+        for (int pp = 0; pp < PPW; ++pp) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int lr = 16 * (h + WPS * j) + 4 * eg + r;
-            const bool ok = lr < nrow && pok && col < sg.ncols;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][ct][r]), orr,
-                                                  ok ? 4 * (lr * (int)sg.ldo + col) : kOOB, 0, 0);
+          for (int ct = 0; ct < 4; ++ct) {
+            const int pl = PPW * pg + pp;
+            const int col = 64 * (panel0 + pl) + 16 * ct + ej;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int lr = 16 * (h + NPH * j) + 4 * eg + r;
+              const bool ok = lr < nrow && pl < npan && col < sg.ncols;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][pp][ct][r]), orr,
+                                                    ok ? 4 * (lr * (int)sg.ldo + col) : kOOB, 0, 0);
+            }
           }
         }
       }
@@ -931,11 +961,11 @@ static bool f8_grouped_ok(const GemmArgs& a, int mode) {
 
 template <int EPI, int TAG>
 static void launch_f8(const GemmArgs& a, hipStream_t s) {
-  constexpr int DA = 2, DB = 3, MT = 12, WPS = 2;
+  constexpr int DA = 2, DB = 3, MT = 12, WPS = 2, PPW = 1;
   const unsigned nblk = (unsigned)ceil_div(a.P, 4);
   const unsigned g8 = (unsigned)ceil_div(a.n_groups, 8) * 8;
-  hipLaunchKernelGGL((tiled_gemm_kernel<A_MXFP8, false, DA, DB, MT, WPS, EPI, TAG>), dim3(g8 * nblk), dim3(256 * WPS),
-                     0, s, a);
+  hipLaunchKernelGGL((tiled_gemm_kernel<A_MXFP8, false, DA, DB, MT, WPS, PPW, EPI, TAG>), dim3(g8 * nblk),
+                     dim3(256 * WPS), 0, s, a);
 }
 
 // Dense bf16 launches with enough rows to fill the chip with 128-row chunks (8 per XCD) take the
@@ -947,11 +977,11 @@ static bool dense_tiled_ok(const GemmArgs& a) {
 
 template <int TAG>
 static void launch_dense_tiled(const GemmArgs& a, hipStream_t s) {
-  constexpr int DA = 2, DB = 2, MT = kDenseRows / 16, WPS = 2;
+  constexpr int DA = 2, DB = 2, MT = kDenseRows / 16, WPS = 2, PPW = 1;
   const unsigned nblk = (unsigned)ceil_div(a.P, 4);
   const unsigned g8 = (unsigned)ceil_div(ceil_div(a.M, kDenseRows), 8) * 8;
-  hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, true, DA, DB, MT, WPS, 2, TAG>), dim3(g8 * nblk), dim3(256 * WPS), 0,
-                     s, a);
+  hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, true, DA, DB, MT, WPS, PPW, 2, TAG>), dim3(g8 * nblk), dim3(256 * WPS),
+                     0, s, a);
 }
 
 hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) {
