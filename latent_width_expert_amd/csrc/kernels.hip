@@ -1037,23 +1037,34 @@ __device__ __forceinline__ u64 topk_pack(float key, int e) {
   return ((u64)ord << 32) | (u64)(0xFFFFFFFFu - (u32)e);
 }
 
+// Maximum of a 64-bit value over the wave with DPP moves (quad swaps, half-row and row mirrors, then
+// the row broadcasts 15 and 31 that carry each row's maximum into the next rows): lane 63 ends with
+// the wave maximum, which readlane makes uniform. Lanes a move does not reach keep their value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ u64 dpp_max_step(u64 v) {
+  const u32 lo = (u32)v, hi = (u32)(v >> 32);
+  const u32 olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false);
+  const u32 ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false);
+  const u64 o = ((u64)ohi << 32) | olo;
+  return o > v ? o : v;
+}
 __device__ __forceinline__ u64 wave_max_u64(u64 v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const u32 lo = __shfl_xor((u32)v, off);
-    const u32 hi = __shfl_xor((u32)(v >> 32), off);
-    const u64 o = ((u64)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_max_step<0x140, 0xF>(v);  // row_mirror: every lane of a row holds the row maximum
+  v = dpp_max_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3: lane 63 holds the maximum
+  const u32 lo = __builtin_amdgcn_readlane((u32)v, 63), hi = __builtin_amdgcn_readlane((u32)(v >> 32), 63);
+  return ((u64)hi << 32) | lo;
 }
 
 template <int NPER>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores, const float* __restrict__ bias,
-                                                   int T, int E, int k, int32_t* __restrict__ idx,
-                                                   float* __restrict__ p) {
+__global__ __launch_bounds__(64) void topk_kernel(const float* __restrict__ scores, const float* __restrict__ bias,
+                                                  int T, int E, int k, int32_t* __restrict__ idx,
+                                                  float* __restrict__ p) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = blockIdx.x;
   if (t >= T) return;  // uniform over the wave
   const float* srow = scores + (int64_t)t * E;
   float sv[NPER], bv[NPER];
@@ -1100,16 +1111,16 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
 
 hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* idx, float* p,
                        hipStream_t s) {
-  dim3 grid((unsigned)ceil_div(T, 4));
+  dim3 grid((unsigned)T);  // one wave per token
   const int nper = (int)ceil_div(E, 64);
   if (nper <= 1)
-    hipLaunchKernelGGL((topk_kernel<1>), grid, dim3(256), 0, s, scores, bias, T, E, k, idx, p);
+    hipLaunchKernelGGL((topk_kernel<1>), grid, dim3(64), 0, s, scores, bias, T, E, k, idx, p);
   else if (nper <= 4)
-    hipLaunchKernelGGL((topk_kernel<4>), grid, dim3(256), 0, s, scores, bias, T, E, k, idx, p);
+    hipLaunchKernelGGL((topk_kernel<4>), grid, dim3(64), 0, s, scores, bias, T, E, k, idx, p);
   else if (nper <= 14)
-    hipLaunchKernelGGL((topk_kernel<14>), grid, dim3(256), 0, s, scores, bias, T, E, k, idx, p);
+    hipLaunchKernelGGL((topk_kernel<14>), grid, dim3(64), 0, s, scores, bias, T, E, k, idx, p);
   else if (nper <= 32)
-    hipLaunchKernelGGL((topk_kernel<32>), grid, dim3(256), 0, s, scores, bias, T, E, k, idx, p);
+    hipLaunchKernelGGL((topk_kernel<32>), grid, dim3(64), 0, s, scores, bias, T, E, k, idx, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
