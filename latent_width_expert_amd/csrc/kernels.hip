@@ -1305,16 +1305,19 @@ hipError_t launch_route(const int32_t* idx, int T, int E, int k, int32_t* counts
 // Combine + RMSNorm (eq. 11): u_t = sum_j p_tj O[inv[t, j]] in selection order, then
 // n_t = bf16(gamma * u_t / sqrt(mean(u_t^2) + eps)). One block per token.
 // ---------------------------------------------------------------------------------------------
-constexpr int kCombineThreads = 1024;
+constexpr int kCombineThreads = 256;
 constexpr int kMaxWidth = 8192;
+constexpr int kCombineChunks = kMaxWidth / (4 * kCombineThreads);  // float4 columns per thread, at most
 
+// One block of 256 threads per token; thread tid holds columns 4 tid + 1024 i (i < 8) of u_t in
+// registers. KC > 0: k fixed at compile time, so all of a chunk's row loads are in flight at once.
+template <int KC>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ O,
                                                                   const int32_t* __restrict__ inv,
                                                                   const float* __restrict__ p, int k, int width,
                                                                   const float* __restrict__ gamma, float eps, int mode,
                                                                   u16* __restrict__ n_out, int64_t ldn,
                                                                   float* __restrict__ u_out) {
-  __shared__ float us[kMaxWidth];
   __shared__ int32_t rows[64];
   __shared__ float pp[64];
   __shared__ float red[kCombineThreads / 64];
@@ -1325,20 +1328,39 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
     pp[tid] = p[(int64_t)t * k + tid];
   }
   __syncthreads();
+  float4 u[kCombineChunks];
   float sq = 0.0f;
-  for (int c = 4 * tid; c < width; c += 4 * kCombineThreads) {
+#pragma unroll
+  for (int i = 0; i < kCombineChunks; ++i) {
+    const int c = 4 * tid + 4 * kCombineThreads * i;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int jj = 0; jj < k; ++jj) {
-      const float4 o = *(const float4*)(O + (int64_t)rows[jj] * width + c);
-      const float w = pp[jj];
-      a.x += w * o.x;
-      a.y += w * o.y;
-      a.z += w * o.z;
-      a.w += w * o.w;
+    if (c < width) {
+      if constexpr (KC > 0) {
+        float4 o[KC];
+#pragma unroll
+        for (int jj = 0; jj < KC; ++jj) o[jj] = *(const float4*)(O + (int64_t)rows[jj] * width + c);
+#pragma unroll
+        for (int jj = 0; jj < KC; ++jj) {  // selection order, as the runtime-k loop
+          const float w = pp[jj];
+          a.x += w * o[jj].x;
+          a.y += w * o[jj].y;
+          a.z += w * o[jj].z;
+          a.w += w * o[jj].w;
+        }
+      } else {
+        for (int jj = 0; jj < k; ++jj) {
+          const float4 o = *(const float4*)(O + (int64_t)rows[jj] * width + c);
+          const float w = pp[jj];
+          a.x += w * o.x;
+          a.y += w * o.y;
+          a.z += w * o.z;
+          a.w += w * o.w;
+        }
+      }
+      if (u_out) *(float4*)(u_out + (int64_t)t * width + c) = a;
+      sq += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
     }
-    *(float4*)(us + c) = a;
-    if (u_out) *(float4*)(u_out + (int64_t)t * width + c) = a;
-    sq += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    u[i] = a;
   }
   if (mode != 0) return;
 #pragma unroll
@@ -1349,16 +1371,31 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
 #pragma unroll
   for (int i = 0; i < kCombineThreads / 64; ++i) tot += red[i];
   const float rs = 1.0f / sqrtf(tot / (float)width + eps);
-  for (int c = tid; c < width; c += kCombineThreads)
-    n_out[(int64_t)t * ldn + c] = (u16)bf16_rne(gamma[c] * us[c] * rs);
+#pragma unroll
+  for (int i = 0; i < kCombineChunks; ++i) {
+    const int c = 4 * tid + 4 * kCombineThreads * i;
+    if (c < width) {
+      const float4 gm = *(const float4*)(gamma + c);
+      const u32 lo = bf16_rne(gm.x * u[i].x * rs) | (bf16_rne(gm.y * u[i].y * rs) << 16);
+      const u32 hi = bf16_rne(gm.z * u[i].z * rs) | (bf16_rne(gm.w * u[i].w * rs) << 16);
+      *(uint2*)(n_out + (int64_t)t * ldn + c) = make_uint2(lo, hi);
+    }
+  }
 }
 
 hipError_t launch_combine(const float* O, const int32_t* inv, const float* p, int T, int k, int width,
                           const float* gamma, float eps, int mode, uint16_t* n_out, int64_t ldn, float* u_out,
                           hipStream_t s) {
-  if (width > kMaxWidth || k > 64 || width % 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(kCombineThreads), 0, s, O, inv, p, k, width, gamma, eps, mode,
-                     n_out, ldn, u_out);
+  if (width > kMaxWidth || k > 64 || width % 4 || (mode == 0 && ldn % 4)) return hipErrorInvalidValue;
+  if (k == 16)
+    hipLaunchKernelGGL(combine_kernel<16>, dim3(T), dim3(kCombineThreads), 0, s, O, inv, p, k, width, gamma, eps, mode,
+                       n_out, ldn, u_out);
+  else if (k == 8)
+    hipLaunchKernelGGL(combine_kernel<8>, dim3(T), dim3(kCombineThreads), 0, s, O, inv, p, k, width, gamma, eps, mode,
+                       n_out, ldn, u_out);
+  else
+    hipLaunchKernelGGL(combine_kernel<0>, dim3(T), dim3(kCombineThreads), 0, s, O, inv, p, k, width, gamma, eps, mode,
+                       n_out, ldn, u_out);
   return hipGetLastError();
 }
 
