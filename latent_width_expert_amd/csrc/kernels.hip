@@ -1002,7 +1002,7 @@ hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) 
       break;
     case GEMM_GATEUP:
       if (a.a_fmt == A_BF16)
-        launch_one<1, A_BF16, 3, 1, true, GEMM_GATEUP>(a, s);
+        launch_one<1, A_BF16, 4, 1, true, GEMM_GATEUP>(a, s);  // weights 3 windows ahead
       else if (f8_grouped_ok(a, EPI_SWIGLU_MXFP8))
         launch_f8<1, GEMM_GATEUP>(a, s);
       else
