@@ -489,7 +489,7 @@ __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_ker
 }
 
 // ---------------------------------------------------------------------------------------------
-// Grouped GEMM on scaled MFMA: MXFP8 activations x MXFP4 weights (many rows per expert).
+// Scaled MFMA operands and LDS-DMA helpers (used by the row-tiled kernel below).
 //
 // v_mfma_scale_f32_16x16x128_f8f6f4 takes E4M3 A and E2M1 B with their E8M0 block scales and
 // accumulates in fp32, so neither operand is converted. Operand lanes (gfx950, established on
@@ -497,11 +497,6 @@ __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_ker
 // [64 + 16 g, 64 + 16 g + 16) of the 128-wide window; fp4 B lane (j, g) holds weight row j, K
 // [32 g, 32 g + 32) -- exactly one lane's 16 bytes of a packed panel-window; the scale operand of
 // lane (r, g) is the scale of row r, K block g (a byte of a 32-bit register chosen by opsel).
-//
-// The weights (one read of each panel-window per row chunk) stream straight into registers,
-// the activation rows shared by the block's waves go through LDS (LDS-DMA, buffer_load ... lds).
-// All loads are issued unconditionally (out-of-range ones read zeros without memory traffic), so
-// one explicit wait count per window covers both streams.
 // ---------------------------------------------------------------------------------------------
 typedef int i32x8 __attribute__((__vector_size__(8 * sizeof(int))));
 
