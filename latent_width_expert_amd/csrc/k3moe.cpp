@@ -47,7 +47,7 @@ struct k3moe_ctx {
   size_t gu_stride = 0, dn_stride = 0;
   // workspace layout (for max_tokens)
   size_t ws_scores = 0, ws_idx = 0, ws_p = 0, ws_counts = 0, ws_offsets = 0, ws_perm = 0, ws_inv = 0, ws_route = 0;
-  size_t ws_z = 0, ws_zs = 0, ws_h = 0, ws_hs = 0, ws_o = 0, ws_abuf = 0, ws_u = 0, ws_total = 0;
+  size_t ws_z = 0, ws_zs = 0, ws_h = 0, ws_hs = 0, ws_o = 0, ws_abuf = 0, ws_u = 0, ws_partial = 0, ws_total = 0;
   // state
   uint8_t* packed = nullptr;
   bool dense_packed = false;
@@ -184,6 +184,7 @@ int k3moe_create(const k3moe_config* cfg, k3moe_ctx** out) {
   x->ws_o = take(4 * T * k * le);
   x->ws_abuf = take(2 * T * (size_t)x->y_K);
   x->ws_u = take(4 * T * le);
+  x->ws_partial = take((size_t)gemm_partial_bytes());
   x->ws_total = w;
   x->routed_packed.assign(E, 0);
   *out = x;
@@ -448,6 +449,8 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     }
     a.nseg = n;
     HIPCHECK(ctx, mark(ST_X, 0), "event");
+    a.partial = (float*)(ws + ctx->ws_partial);
+    a.partial_bytes = gemm_partial_bytes();
     HIPCHECK(ctx, launch_panel_gemm(a, GEMM_X, s), "x_gemm launch");
     HIPCHECK(ctx, mark(ST_X, 1), "event");
   }
@@ -570,6 +573,8 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     sg.addend = u;
     sg.ldadd = d;
     a.nseg = 1;
+    a.partial = (float*)(ws + ctx->ws_partial);
+    a.partial_bytes = gemm_partial_bytes();
     HIPCHECK(ctx, launch_panel_gemm(a, GEMM_Y, s), "y_gemm launch");
   } else {
     HIPCHECK(ctx, launch_f32_to_bf16(u, (uint16_t*)y_dev, (int64_t)T * d, s), "y convert launch");

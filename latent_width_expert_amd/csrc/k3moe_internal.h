@@ -99,6 +99,8 @@ struct GemmArgs {
   int32_t many_rows;       // grouped: rows per group large enough for the LDS-tiled scaled-MFMA kernel
   int32_t nseg;
   EpiSeg seg[kMaxSeg];
+  float* partial;          // dense launches of few rows: split-K partial sums (workspace), may be null
+  int64_t partial_bytes;   // at least gemm_partial_bytes() to be used
 };
 
 enum GemmStage : int { GEMM_X = 0, GEMM_GATEUP = 1, GEMM_DOWN = 2, GEMM_Y = 3 };
@@ -106,6 +108,8 @@ enum GemmStage : int { GEMM_X = 0, GEMM_GATEUP = 1, GEMM_DOWN = 2, GEMM_Y = 3 };
 hipError_t launch_pack(const PackJob& job, hipStream_t s);
 // Grouped launches (offsets != null) use n_groups blocks along y; dense launches cover M rows.
 hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s);
+// workspace for the split-K partial sums of dense launches of at most 64 rows
+int64_t gemm_partial_bytes();
 hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* idx, float* p,
                        hipStream_t s);
 // scratch: route_scratch_bytes(max_tokens, E) bytes of workspace (per-chunk expert counts); small T

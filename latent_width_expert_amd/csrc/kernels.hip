@@ -7,6 +7,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -691,8 +692,10 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
         const bool real = wa >= 0;
         const bool in = real && wa < nwin;
         const u32 st = (u32)((wa % NA) * A_STAGE);
-        if constexpr (d < APW)
-          dma16<false>(ar, real ? a_w + st + 1024 * d : lds_s,
+        if (!real)
+          dma4<false>(ar, lds_s, kOOB);  // prologue placeholder (4 bytes a lane: the sink holds 256)
+        else if constexpr (d < APW)
+          dma16<false>(ar, a_w + st + 1024 * d,
                        in && acode[d] >= 0 && kWinK * wa + akel[d] < args.K ? acode[d] + AROW * wa : kOOB);
         else
           dma4<false>(asr, real ? a_s + st : lds_s, in && ascale >= 0 ? ascale + 4 * wa : kOOB);
@@ -927,6 +930,230 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
 }
 
 
+// Skinny dense GEMM (at most 64 rows, e.g. a decode batch against x's or the output's weights).
+// With few rows the weights are the whole stream and the activation tile is small but needed by
+// every panel; a wave per panel would re-read it once per panel. Here a block of 8 waves takes 4
+// panels (one panel block) and shares each activation window among them through LDS, and the
+// panel-block windows (nblk x nwin of them) are dealt to kSkinnyBlocks blocks as equal contiguous
+// ranges of that flattened sequence (split-K across blocks), so every CU streams the same share of
+// weights whatever the panel count. A range covers at most two panel blocks (the host keeps ranges
+// no longer than a panel); its DMAs run continuously across the boundary, the two segments keep
+// separate fp32 accumulators and each is written as a partial tile to workspace slot
+// 2 * block + segment. skinny_reduce_kernel then sums, for each panel, the partials of the
+// blocks that cover it in block order (deterministic) and applies the panel's segment epilogue.
+// Wave (pl, h): panel pl of the block, row tiles h and h + 2. Per window, as in the row-tiled
+// kernel: activation rows (LDS-DMA, DA windows ahead, 16-byte chunks XOR-swizzled by row) and the
+// four panel-windows (non-temporal LDS-DMA, DB ahead), one wait and one barrier per window, the
+// wave's weights converted to bf16 operands once per window.
+// Partial slot layout (fp32, MFMA order): [4 row tiles][4 panels][4 column tiles][64 lanes][4].
+constexpr int kSkinnyBlocks = 256;  // one block per CU
+constexpr int kSkinnyRows = 64;
+constexpr int64_t kSkinnySlotBytes = 4 * 4 * 4 * 64 * 16;
+
+template <int DA, int DB, int TAG>
+__global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmArgs args) {
+  constexpr int NWAVE = 8, NA = DA + 1, NB = DB + 1;
+  constexpr int AROW = 256, CPR = 16, RPD = 4;  // bf16 row window: 256 bytes; 4 rows per 1 KB DMA
+  constexpr int A_STAGE = kSkinnyRows * AROW;
+  constexpr int B_STAGE = 4 * kPanelWinBytes;
+  constexpr int APW = kSkinnyRows / RPD / NWAVE;  // 2
+  constexpr int BPW = 3;                          // 20 weight DMAs over 8 waves, 4 dummies
+  constexpr int LPW = APW + BPW;
+  constexpr int WAITN = (DB > DA ? BPW : 0) + (DA - 1) * LPW;  // as in the row-tiled kernel
+  static_assert(DB >= DA && DA >= 1 && WAITN < 64, "ring depths");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[NA][A_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[NB][B_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sink[NWAVE][256];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pl = wv % 4, h = wv / 4;
+  const int nwin = args.wwin, P = args.P;
+  const int nblk = (P + 3) / 4;
+  const int G = gridDim.x, b = blockIdx.x;
+  const int64_t U = (int64_t)nblk * nwin;
+  const int u0 = (int)((int64_t)b * U / G), u1 = (int)((int64_t)(b + 1) * U / G);
+  if (u0 >= u1) return;
+  const int n = u1 - u0;
+  const int q0 = u0 / nwin, w0 = u0 - q0 * nwin;
+  const int n0 = min(n, nwin - w0);  // windows of the first segment; the rest start panel block q0 + 1
+
+  const i32x4s wr = sgpr_rsrc(args.W, (int64_t)P * nwin * kPanelWinBytes);
+  const i32x4s ar = sgpr_rsrc(args.A, args.a_bytes);
+  const int g = lane >> 4, i16 = lane & 15;
+  const u32 lds_a0 = lds_addr(&lds_a[0][0]), lds_b0 = lds_addr(&lds_b[0][0]);
+  const u32 lds_s = lds_addr(&lds_sink[wv][0]);
+
+  // A code DMA jj of this wave covers rows RPD (wv APW + jj) .. + RPD - 1 (lane L: row + L / CPR,
+  // position L % CPR holding chunk (L % CPR) ^ (row & 7)); rows past M read zeros
+  int acode[APW], akel[APW];
+#pragma unroll
+  for (int jj = 0; jj < APW; ++jj) {
+    const int r = RPD * (wv * APW + jj) + lane / CPR;
+    const int c = (lane % CPR) ^ (r & 7);
+    akel[jj] = 8 * c;
+    acode[jj] = r < args.M ? r * (int)args.lda * 2 + 16 * c : -1;
+  }
+  const u32 a_w = lds_a0 + 1024 * (wv * APW);
+  // window of the block's local step j
+  auto qw = [&](int j, int& q, int& w) {
+    q = j < n0 ? q0 : q0 + 1;
+    w = j < n0 ? w0 + j : j - n0;
+  };
+  auto issue_one = [&]<int d>(int i) {
+    if constexpr (d < APW) {
+      const int ja = i + DA;
+      const bool real = ja >= 0, in = real && ja < n;
+      int q, w;
+      qw(ja, q, w);
+      if (!real) {
+        dma4<false>(ar, lds_s, kOOB);  // prologue placeholder: keeps the per-step DMA count
+      } else {
+        const u32 st = (u32)((ja % NA) * A_STAGE);
+        dma16<false>(ar, a_w + st + 1024 * d,
+                     in && acode[d] >= 0 && kWinK * w + akel[d] < args.K ? acode[d] + AROW * w : kOOB);
+      }
+    } else {
+      const int jb = i + DB;  // >= 0
+      const int item = wv * BPW + (d - APW);
+      const int p = item / 5, piece = item % 5;
+      int q, w;
+      qw(jb, q, w);
+      const int panel = 4 * q + p;
+      const bool in = jb < n && panel < P;
+      const u32 st = lds_b0 + (u32)((jb % NB) * B_STAGE + p * kPanelWinBytes);
+      const int src = (panel * nwin + w) * kPanelWinBytes;
+      if (item >= 20)
+        dma4<false>(wr, lds_s, kOOB);
+      else if (piece < 4)
+        dma16<true>(wr, st + 1024 * piece, in ? src + 1024 * piece + lane * 16 : kOOB);
+      else
+        dma4<true>(wr, st + 4096, in ? src + 4096 + lane * 4 : kOOB);
+    }
+  };
+  auto issue_range = [&]<int D0, int D1>(int i) {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (issue_one.template operator()<D0 + I>(i), ...);
+    }(std::make_integer_sequence<int, D1 - D0>{});
+  };
+
+  const int nt = (min(args.M, kSkinnyRows) + 15) / 16;
+  const int nw = (nt > h ? 1 : 0) + (nt > h + 2 ? 1 : 0);  // the wave's row tiles holding rows
+  f32x4 acc0[2][4], acc1[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc0[j][ct] = acc1[j][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto run = [&]<int N>() {
+    for (int i = -DB; i < 0; ++i) issue_range.template operator()<0, LPW>(i);
+    auto step = [&](int i, f32x4(&acc)[2][4]) {
+      wait_vmcnt<WAITN>();
+      barrier_nowait();  // stages of step i complete for every wave; stages of i - 1 free
+      const uint8_t* sb = &lds_b[i % NB][pl * kPanelWinBytes];
+      u32x4 bw[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) bw[ct] = *(const u32x4*)(sb + ct * 1024 + lane * 16);
+      const u32 bsc = *(const u32*)(sb + 4096 + lane * 4);
+      const uint8_t* prow = lds_a[i % NA] + i16 * AROW + h * 16 * AROW;
+      auto load_tile = [&](int j, u32x4(&aop)[4]) {  // row tile h + 2 j; lane (i16, g), step st: K [32 g + 8 st, +8)
+        const uint8_t* pr = prow + j * 2 * 16 * AROW;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) aop[st] = *(const u32x4*)(pr + 16 * ((4 * g + st) ^ (i16 & 7)));
+      };
+      if constexpr (N == 0) {
+        issue_range.template operator()<0, LPW>(i);
+      } else {
+        bf16x8 bcv[4][4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int st = 0; st < 4; ++st) bcv[ct][st] = fp4_operand(bw[ct][st], e8m0_f32((bsc >> (8 * ct)) & 0xFFu));
+        u32x4 cur[4];
+        load_tile(0, cur);
+        [&]<int... JI>(std::integer_sequence<int, JI...>) {
+          ([&] {
+            constexpr int j = JI;
+            u32x4 nxt[4];
+            if constexpr (j + 1 < N) load_tile(j + 1, nxt);
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+              const bf16x8 av = __builtin_bit_cast(bf16x8, cur[st]);
+#pragma unroll
+              for (int ct = 0; ct < 4; ++ct)
+                acc[j][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bcv[ct][st], acc[j][ct], 0, 0, 0);
+            }
+            issue_range.template operator()<j * LPW / N, (j + 1) * LPW / N>(i);
+            if constexpr (j + 1 < N) {
+#pragma unroll
+              for (int st = 0; st < 4; ++st) cur[st] = nxt[st];
+            }
+          }(), ...);
+        }(std::make_integer_sequence<int, N>{});
+      }
+    };
+    int i = 0;
+    for (; i < n0; ++i) step(i, acc0);
+    for (; i < n; ++i) step(i, acc1);
+  };
+  if (nw == 2)
+    run.template operator()<2>();
+  else if (nw == 1)
+    run.template operator()<1>();
+  else
+    run.template operator()<0>();
+  wait_vmcnt<0>();
+
+  // partial tiles: slot 2 b (+1 for the second segment), [tile][panel][column tile][lane] f32x4
+  const rsrc_t prr = make_rsrc(args.partial, args.partial_bytes);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (j < nw) {
+      const int t = h + 2 * j;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int o = (((t * 4 + pl) * 4 + ct) * 64 + lane) * 16;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc0[j][ct]), prr,
+                                               (int)((2 * b) * kSkinnySlotBytes) + o, 0, 0);
+        if (n > n0)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc1[j][ct]), prr,
+                                                 (int)((2 * b + 1) * kSkinnySlotBytes) + o, 0, 0);
+      }
+    }
+  }
+}
+
+// Sum of the partial tiles of one (panel block, row tile) in block order, then the panel's segment
+// epilogue. Block: 4 waves, wave p = panel p of panel block blockIdx.x, row tile blockIdx.y.
+template <int TAG>
+__global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs args, int G) {
+  const int lane = threadIdx.x & 63;
+  const int p = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = blockIdx.x, t = blockIdx.y;
+  const int panel = 4 * q + p;
+  if (panel >= args.P) return;
+  const int nwin = args.wwin;
+  const int64_t U = (int64_t)((args.P + 3) / 4) * nwin;
+  const int64_t ua = (int64_t)q * nwin, ue = ua + nwin;
+  // the last block whose range starts at or before ua: ranges start at floor(b U / G)
+  int b = (int)(((ua + 1) * G + U - 1) / U) - 1;
+  const rsrc_t prr = make_rsrc(args.partial, args.partial_bytes);
+  f32x4 acc[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (; b < G; ++b) {
+    const int64_t u0 = (int64_t)b * U / G, u1 = (int64_t)(b + 1) * U / G;
+    if (u0 >= ue) break;
+    if (u1 <= u0 || u1 <= ua) continue;
+    const int seg = q - (int)(u0 / nwin);  // 0: the range starts in this panel block, 1: in the previous one
+    const int base = (int)((2 * b + seg) * kSkinnySlotBytes) + ((t * 4 + p) * 4 * 64 + lane) * 16;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      acc[ct] += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prr, base + ct * 1024, 0, 0));
+  }
+  epilogue(args, acc, panel, 16 * t, min(args.M, kSkinnyRows), lane);
+}
+
 template <int KSPLIT, int AFMT, int NBUF, int MT, bool AHEAD, int TAG>
 static void launch_one(GemmArgs a, hipStream_t s) {
   constexpr int ppb = BlockShape<KSPLIT>::panels;
@@ -979,18 +1206,40 @@ static void launch_dense_tiled(const GemmArgs& a, hipStream_t s) {
                      0, s, a);
 }
 
+// Dense bf16 launches of at most 64 rows take the split-K skinny kernel when the workspace for its
+// partial sums is there and the panel blocks fit the block count (ranges no longer than a panel).
+int64_t gemm_partial_bytes() { return 2 * kSkinnyBlocks * kSkinnySlotBytes; }
+static bool skinny_ok(const GemmArgs& a) {
+  return !a.offsets && a.a_fmt == A_BF16 && a.M <= kSkinnyRows && a.lda % 8 == 0 && a.K % 32 == 0 &&
+         a.partial && a.partial_bytes >= gemm_partial_bytes() && ceil_div(a.P, 4) <= kSkinnyBlocks &&
+         a.a_bytes < (int64_t)1 << 30 && (int64_t)a.P * a.wwin * kPanelWinBytes < (int64_t)1 << 30;
+}
+
+template <int TAG>
+static void launch_skinny(const GemmArgs& a, hipStream_t s) {
+  constexpr int DA = 2, DB = 4;
+  const int nblk = (int)ceil_div(a.P, 4);
+  const int G = (int)std::min<int64_t>(kSkinnyBlocks, (int64_t)nblk * a.wwin);  // nblk <= G <= windows
+  hipLaunchKernelGGL((skinny_gemm_kernel<DA, DB, TAG>), dim3(G), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((skinny_reduce_kernel<TAG>), dim3(nblk, (unsigned)ceil_div(a.M, 16)), dim3(256), 0, s, a, G);
+}
+
 hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) {
   if (a.P <= 0) return hipSuccess;
   if (a.offsets == nullptr && a.M <= 0) return hipSuccess;
   switch (stage) {
     case GEMM_X:
-      if (dense_tiled_ok(a))
+      if (skinny_ok(a))
+        launch_skinny<GEMM_X>(a, s);
+      else if (dense_tiled_ok(a))
         launch_dense_tiled<GEMM_X>(a, s);
       else
         launch_one<8, A_BF16, 3, 1, true, GEMM_X>(a, s);
       break;
     case GEMM_Y:
-      if (dense_tiled_ok(a))
+      if (skinny_ok(a))
+        launch_skinny<GEMM_Y>(a, s);
+      else if (dense_tiled_ok(a))
         launch_dense_tiled<GEMM_Y>(a, s);
       else
         launch_one<8, A_BF16, 3, 1, true, GEMM_Y>(a, s);
