@@ -16,6 +16,7 @@ namespace k3 {
 typedef uint32_t u32;
 typedef uint16_t u16;
 typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
@@ -931,60 +932,66 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
 
 
 // Skinny dense GEMM (at most 64 rows, e.g. a decode batch against x's or the output's weights).
-// With few rows the weights are the whole stream and the activation tile is small but needed by
-// every panel; a wave per panel would re-read it once per panel. Here a block of 8 waves takes 4
-// panels (one panel block) and shares each activation window among them through LDS, and the
-// panel-block windows (nblk x nwin of them) are dealt to kSkinnyBlocks blocks as equal contiguous
-// ranges of that flattened sequence (split-K across blocks), so every CU streams the same share of
-// weights whatever the panel count. A range covers at most two panel blocks (the host keeps ranges
-// no longer than a panel); its DMAs run continuously across the boundary, the two segments keep
-// separate fp32 accumulators and each is written as a partial tile to workspace slot
-// 2 * block + segment. skinny_reduce_kernel then sums, for each panel, the partials of the
-// blocks that cover it in block order (deterministic) and applies the panel's segment epilogue.
-// Wave (pl, h): panel pl of the block, row tiles h and h + 2. Per window, as in the row-tiled
-// kernel: activation rows (LDS-DMA, DA windows ahead, 16-byte chunks XOR-swizzled by row) and the
-// four panel-windows (non-temporal LDS-DMA, DB ahead), one wait and one barrier per window, the
-// wave's weights converted to bf16 operands once per window.
-// Partial slot layout (fp32, MFMA order): [4 row tiles][4 panels][4 column tiles][64 lanes][4].
+// With few rows the weights are the whole stream and the activation window (64 rows x 128 K) is
+// needed by every panel; fetched per panel it would cost several times the weights. A block of 8
+// waves takes one panel block (4 panels); wave (p, kh) computes panel p over all row tiles for
+// half of every K window (MFMA steps 2 kh, 2 kh + 1), so each weight is converted to a bf16
+// operand once and two waves share each SIMD (one wave alone issues the bf16 MFMA at about half
+// its rate). Each activation window goes to LDS once (LDS-DMA, 16-byte chunks XOR-swizzled by
+// row) and is read by all eight waves; each wave streams its half panel-windows straight into a
+// register ring (non-temporal loads). Both rings run DA windows ahead: loads complete in order, so
+// waiting for an activation window also waits for every weight load issued before it.
+// Split-K across blocks: the nblk x nwin panel-block windows, in that order, are dealt to the
+// grid as equal contiguous ranges (never longer than a panel), so every CU streams the same share
+// of weights whatever the panel count. A range covers at most two panel blocks; its loads run on
+// across the boundary, and the sums of each segment (the two K halves added through LDS) are
+// written as a partial tile to workspace slot 2 * block + segment (fp32, MFMA order: [4 row
+// tiles][4 panels][4 column tiles][64 lanes] x 4). skinny_reduce_kernel then adds, for each panel,
+// the partials of the blocks that cover it in block order (deterministic) and applies the panel's
+// segment epilogue.
 constexpr int kSkinnyBlocks = 256;  // one block per CU
 constexpr int kSkinnyRows = 64;
 constexpr int64_t kSkinnySlotBytes = 4 * 4 * 4 * 64 * 16;
 
-template <int DA, int DB, int TAG>
+template <int DA, int NB, int TAG>
 __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmArgs args) {
-  constexpr int NWAVE = 8, NA = DA + 1, NB = DB + 1;
+  constexpr int NA = DA + 1, DB = NB - 1;
   constexpr int AROW = 256, CPR = 16, RPD = 4;  // bf16 row window: 256 bytes; 4 rows per 1 KB DMA
   constexpr int A_STAGE = kSkinnyRows * AROW;
-  constexpr int B_STAGE = 4 * kPanelWinBytes;
-  constexpr int APW = kSkinnyRows / RPD / NWAVE;  // 2
-  constexpr int BPW = 3;                          // 20 weight DMAs over 8 waves, 4 dummies
+  constexpr int APW = kSkinnyRows / RPD / 8;    // 2 activation DMAs per wave and step
+  constexpr int BPW = 5;                        // the wave's half panel-window: four 8-byte and one 4-byte load
   constexpr int LPW = APW + BPW;
-  constexpr int WAITN = (DB > DA ? BPW : 0) + (DA - 1) * LPW;  // as in the row-tiled kernel
+  // At step i the later of A(i) and B(i) must have landed (loads complete in order). DB > DA: A(i)
+  // is the later one, followed by its step's weight loads and DA - 1 full steps; DB == DA: B(i)
+  // comes last in its step, followed by DA - 1 full steps. Waiting for A(i) also waits for every
+  // weight load issued before it, so the weights stay only DA - 1 windows ahead whatever DB is:
+  // both rings are kept equally deep.
+  constexpr int WAITN = (DB > DA ? BPW : 0) + (DA - 1) * LPW;
   static_assert(DB >= DA && DA >= 1 && WAITN < 64, "ring depths");
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[NA][A_STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[NB][B_STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_sink[NWAVE][256];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sink[8][256];
+  __shared__ __attribute__((aligned(16))) f32x4 lds_x[4][4][4][64];  // K-half sums handed over at segment ends
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int pl = wv % 4, h = wv / 4;
+  const int pw = wv & 3, kh = wv >> 2;  // panel of the block; K half of every window (MFMA steps 2 kh, 2 kh + 1)
   const int nwin = args.wwin, P = args.P;
   const int nblk = (P + 3) / 4;
   const int G = gridDim.x, b = blockIdx.x;
-  const int64_t U = (int64_t)nblk * nwin;
-  const int u0 = (int)((int64_t)b * U / G), u1 = (int)((int64_t)(b + 1) * U / G);
-  if (u0 >= u1) return;
+  const u32 U = (u32)(nblk * nwin);  // U (G + 1) < 2^31 (host check): 32-bit divisions
+  const int u0 = (int)((u32)b * U / (u32)G), u1 = (int)((u32)(b + 1) * U / (u32)G);
+  if (u0 >= u1) return;  // uniform; never taken with G <= U
   const int n = u1 - u0;
-  const int q0 = u0 / nwin, w0 = u0 - q0 * nwin;
+  const int q0 = (int)((u32)u0 / (u32)nwin), w0 = u0 - q0 * nwin;
   const int n0 = min(n, nwin - w0);  // windows of the first segment; the rest start panel block q0 + 1
 
-  const i32x4s wr = sgpr_rsrc(args.W, (int64_t)P * nwin * kPanelWinBytes);
+  const rsrc_t wr = make_rsrc(args.W, (int64_t)P * nwin * kPanelWinBytes);
   const i32x4s ar = sgpr_rsrc(args.A, args.a_bytes);
   const int g = lane >> 4, i16 = lane & 15;
-  const u32 lds_a0 = lds_addr(&lds_a[0][0]), lds_b0 = lds_addr(&lds_b[0][0]);
+  const u32 lds_a0 = lds_addr(&lds_a[0][0]);
   const u32 lds_s = lds_addr(&lds_sink[wv][0]);
 
-  // A code DMA jj of this wave covers rows RPD (wv APW + jj) .. + RPD - 1 (lane L: row + L / CPR,
+  // activation DMA jj of this wave covers rows RPD (wv APW + jj) .. + RPD - 1 (lane L: row + L / CPR,
   // position L % CPR holding chunk (L % CPR) ^ (row & 7)); rows past M read zeros
   int acode[APW], akel[APW];
 #pragma unroll
@@ -995,136 +1002,153 @@ __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmArgs args) {
     acode[jj] = r < args.M ? r * (int)args.lda * 2 + 16 * c : -1;
   }
   const u32 a_w = lds_a0 + 1024 * (wv * APW);
-  // window of the block's local step j
-  auto qw = [&](int j, int& q, int& w) {
+  auto qw = [&](int j, int& q, int& w) {  // panel block and window of local step j
     q = j < n0 ? q0 : q0 + 1;
     w = j < n0 ? w0 + j : j - n0;
   };
-  auto issue_one = [&]<int d>(int i) {
-    if constexpr (d < APW) {
-      const int ja = i + DA;
-      const bool real = ja >= 0, in = real && ja < n;
+  auto issue_a = [&](int i) {  // activation DMAs of step i + DA (placeholders in the prologue)
+    const int ja = i + DA;
+    if (ja < 0) {
+#pragma unroll
+      for (int jj = 0; jj < APW; ++jj) dma4<false>(ar, lds_s, kOOB);
+    } else {
       int q, w;
       qw(ja, q, w);
-      if (!real) {
-        dma4<false>(ar, lds_s, kOOB);  // prologue placeholder: keeps the per-step DMA count
-      } else {
-        const u32 st = (u32)((ja % NA) * A_STAGE);
-        dma16<false>(ar, a_w + st + 1024 * d,
-                     in && acode[d] >= 0 && kWinK * w + akel[d] < args.K ? acode[d] + AROW * w : kOOB);
-      }
-    } else {
-      const int jb = i + DB;  // >= 0
-      const int item = wv * BPW + (d - APW);
-      const int p = item / 5, piece = item % 5;
-      int q, w;
-      qw(jb, q, w);
-      const int panel = 4 * q + p;
-      const bool in = jb < n && panel < P;
-      const u32 st = lds_b0 + (u32)((jb % NB) * B_STAGE + p * kPanelWinBytes);
-      const int src = (panel * nwin + w) * kPanelWinBytes;
-      if (item >= 20)
-        dma4<false>(wr, lds_s, kOOB);
-      else if (piece < 4)
-        dma16<true>(wr, st + 1024 * piece, in ? src + 1024 * piece + lane * 16 : kOOB);
-      else
-        dma4<true>(wr, st + 4096, in ? src + 4096 + lane * 4 : kOOB);
+      const u32 st = (u32)((ja % NA) * A_STAGE);
+#pragma unroll
+      for (int jj = 0; jj < APW; ++jj)
+        dma16<false>(ar, a_w + st + 1024 * jj,
+                     ja < n && acode[jj] >= 0 && kWinK * w + akel[jj] < args.K ? acode[jj] + AROW * w : kOOB);
     }
   };
-  auto issue_range = [&]<int D0, int D1>(int i) {
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      (issue_one.template operator()<D0 + I>(i), ...);
-    }(std::make_integer_sequence<int, D1 - D0>{});
+  struct HalfWin {  // the wave's half of a panel-window: dwords 2 kh, 2 kh + 1 of every lane's 16 bytes
+    u32x2 c[4];
+    u32 sc;
+  };
+  auto load_b = [&](HalfWin& bb, int j) {  // step j (zeros past the range)
+    int q, w;
+    qw(j, q, w);
+    const int panel = 4 * q + pw;
+    const int off = j < n && panel < P ? (panel * nwin + w) * kPanelWinBytes : kOOB;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+      bb.c[rt] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(wr, off + rt * 1024 + lane * 16 + 8 * kh, 0, kNT));
+    bb.sc = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 4096 + lane * 4, 0, kNT);
   };
 
   const int nt = (min(args.M, kSkinnyRows) + 15) / 16;
-  const int nw = (nt > h ? 1 : 0) + (nt > h + 2 ? 1 : 0);  // the wave's row tiles holding rows
-  f32x4 acc0[2][4], acc1[2][4];
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc0[j][ct] = acc1[j][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto run = [&]<int N>() {
-    for (int i = -DB; i < 0; ++i) issue_range.template operator()<0, LPW>(i);
-    auto step = [&](int i, f32x4(&acc)[2][4]) {
-      wait_vmcnt<WAITN>();
-      barrier_nowait();  // stages of step i complete for every wave; stages of i - 1 free
-      const uint8_t* sb = &lds_b[i % NB][pl * kPanelWinBytes];
-      u32x4 bw[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) bw[ct] = *(const u32x4*)(sb + ct * 1024 + lane * 16);
-      const u32 bsc = *(const u32*)(sb + 4096 + lane * 4);
-      const uint8_t* prow = lds_a[i % NA] + i16 * AROW + h * 16 * AROW;
-      auto load_tile = [&](int j, u32x4(&aop)[4]) {  // row tile h + 2 j; lane (i16, g), step st: K [32 g + 8 st, +8)
-        const uint8_t* pr = prow + j * 2 * 16 * AROW;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) aop[st] = *(const u32x4*)(pr + 16 * ((4 * g + st) ^ (i16 & 7)));
-      };
-      if constexpr (N == 0) {
-        issue_range.template operator()<0, LPW>(i);
-      } else {
-        bf16x8 bcv[4][4];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-          for (int st = 0; st < 4; ++st) bcv[ct][st] = fp4_operand(bw[ct][st], e8m0_f32((bsc >> (8 * ct)) & 0xFFu));
-        u32x4 cur[4];
-        load_tile(0, cur);
-        [&]<int... JI>(std::integer_sequence<int, JI...>) {
-          ([&] {
-            constexpr int j = JI;
-            u32x4 nxt[4];
-            if constexpr (j + 1 < N) load_tile(j + 1, nxt);
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-              const bf16x8 av = __builtin_bit_cast(bf16x8, cur[st]);
-#pragma unroll
-              for (int ct = 0; ct < 4; ++ct)
-                acc[j][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bcv[ct][st], acc[j][ct], 0, 0, 0);
-            }
-            issue_range.template operator()<j * LPW / N, (j + 1) * LPW / N>(i);
-            if constexpr (j + 1 < N) {
-#pragma unroll
-              for (int st = 0; st < 4; ++st) cur[st] = nxt[st];
-            }
-          }(), ...);
-        }(std::make_integer_sequence<int, N>{});
-      }
-    };
-    int i = 0;
-    for (; i < n0; ++i) step(i, acc0);
-    for (; i < n; ++i) step(i, acc1);
-  };
-  if (nw == 2)
-    run.template operator()<2>();
-  else if (nw == 1)
-    run.template operator()<1>();
-  else
-    run.template operator()<0>();
-  wait_vmcnt<0>();
-
-  // partial tiles: slot 2 b (+1 for the second segment), [tile][panel][column tile][lane] f32x4
+    for (int ct = 0; ct < 4; ++ct) acc[t][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   const rsrc_t prr = make_rsrc(args.partial, args.partial_bytes);
+  auto slot_off = [&](int slot, int t, int ct) { return (int)(slot * kSkinnySlotBytes) + (((t * 4 + pw) * 4 + ct) * 64 + lane) * 16; };
+  // the accumulated segment out as a partial tile (upper K half handed to the lower through LDS);
+  // accumulators cleared
+  auto flush = [&](int slot) {
+    if (kh == 1) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (j < nw) {
-      const int t = h + 2 * j;
+      for (int t = 0; t < 4; ++t)
+        if (t < nt) {
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int o = (((t * 4 + pl) * 4 + ct) * 64 + lane) * 16;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc0[j][ct]), prr,
-                                               (int)((2 * b) * kSkinnySlotBytes) + o, 0, 0);
-        if (n > n0)
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc1[j][ct]), prr,
-                                                 (int)((2 * b + 1) * kSkinnySlotBytes) + o, 0, 0);
+          for (int ct = 0; ct < 4; ++ct) lds_x[pw][t][ct][lane] = acc[t][ct];
+        }
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < nt) {
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[t][ct] + lds_x[pw][t][ct][lane]), prr,
+                                                   slot_off(slot, t, ct), 0, 0);
+        }
       }
     }
-  }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[t][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  HalfWin ring[NB];
+  auto run = [&]<int NT>() {
+    // prologue: steps -DB .. -1 in steady-state order (activation DMAs, then weight loads)
+#pragma unroll
+    for (int i = -DB; i < 0; ++i) {
+      issue_a(i);
+      load_b(ring[i + DB], i + DB);
+    }
+    // one step: wait for its activation window, the MFMAs (guarded: steps past the range only keep
+    // the load pattern), then the loads of step i + DA / i + DB (unconditionally, so that the
+    // compiler's own waits for the ring stay exact)
+    auto compute = [&]<int u>(int i) {
+      const HalfWin& cb = ring[u];
+      const uint8_t* prow = lds_a[i % NA] + i16 * AROW;
+      // row tile t, lane (i16, g), MFMA step st = 2 kh + s: K elements [32 g + 8 st, +8); the next
+      // step's operands are read from LDS while this step's MFMAs run
+      auto aload = [&](int t, int s) {
+        return *(const u32x4*)(prow + t * 16 * AROW + 16 * ((4 * g + 2 * kh + s) ^ (i16 & 7)));
+      };
+      u32x4 a_cur[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) a_cur[t] = aload(t, 0);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        u32x4 a_nxt[NT];
+        if (st < 1) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) a_nxt[t] = aload(t, st + 1);
+        }
+        bf16x8 bv[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) bv[ct] = fp4_operand(cb.c[ct][st], e8m0_f32((cb.sc >> (8 * ct)) & 0xFFu));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const bf16x8 av = __builtin_bit_cast(bf16x8, a_cur[t]);
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) acc[t][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[ct], acc[t][ct], 0, 0, 0);
+        }
+        if (st < 1) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) a_cur[t] = a_nxt[t];
+        }
+      }
+    };
+    for (int i0 = 0; i0 < n; i0 += NB) {
+      [&]<int... UI>(std::integer_sequence<int, UI...>) {
+        ([&] {
+          const int i = i0 + UI;
+          wait_vmcnt<WAITN>();
+          barrier_nowait();  // A(i) complete for every wave; the stage of step i - 1 is free
+          if (i < n) compute.template operator()<UI>(i);
+          // issued after the step's MFMAs, so that a full memory queue stalls the wave while the
+          // matrix core works (the wave issues nothing else until the next wait)
+          issue_a(i);
+          load_b(ring[(UI + DB) % NB], i + DB);  // into the slot step i - 1 used
+          if (i == n0 - 1 && n > n0) flush(2 * b);  // end of the first of two segments
+        }(), ...);
+      }(std::make_integer_sequence<int, NB>{});
+    }
+  };
+  if (nt == 4)
+    run.template operator()<4>();
+  else if (nt == 3)
+    run.template operator()<3>();
+  else if (nt == 2)
+    run.template operator()<2>();
+  else
+    run.template operator()<1>();
+  flush(n > n0 ? 2 * b + 1 : 2 * b);
 }
 
 // Sum of the partial tiles of one (panel block, row tile) in block order, then the panel's segment
-// epilogue. Block: 4 waves, wave p = panel p of panel block blockIdx.x, row tile blockIdx.y.
+// epilogue. Block: 4 waves, wave p = panel p of panel block blockIdx.x, row tile blockIdx.y. The
+// covering blocks are consecutive; their partials are loaded kSkinnyBatch at a time (all loads of
+// a batch in flight, blocks past the last one read zeros) and added in block order.
+constexpr int kSkinnyBatch = 8;
 template <int TAG>
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs args, int G) {
   const int lane = threadIdx.x & 63;
@@ -1133,23 +1157,33 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs args, int G
   const int panel = 4 * q + p;
   if (panel >= args.P) return;
   const int nwin = args.wwin;
-  const int64_t U = (int64_t)((args.P + 3) / 4) * nwin;
-  const int64_t ua = (int64_t)q * nwin, ue = ua + nwin;
-  // the last block whose range starts at or before ua: ranges start at floor(b U / G)
-  int b = (int)(((ua + 1) * G + U - 1) / U) - 1;
+  const u32 U = (u32)(((args.P + 3) / 4) * nwin);  // U (G + 1) < 2^31 (host check): 32-bit divisions
+  const u32 ua = (u32)(q * nwin), ue = ua + (u32)nwin;
+  // first and last block whose range meets [ua, ue): block(u) = the last block starting at or before
+  // u (ranges start at floor(b U / G) and are never empty); only the first can start in the previous
+  // panel block
+  const int b_lo = (int)(((ua + 1) * (u32)G + U - 1) / U) - 1;
+  const int b_hi = (int)((ue * (u32)G + U - 1) / U) - 1;
+  const int seg_lo = (u32)b_lo * U / (u32)G < ua ? 1 : 0;
   const rsrc_t prr = make_rsrc(args.partial, args.partial_bytes);
+  const int lo = ((t * 4 + p) * 4 * 64 + lane) * 16;
   f32x4 acc[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (; b < G; ++b) {
-    const int64_t u0 = (int64_t)b * U / G, u1 = (int64_t)(b + 1) * U / G;
-    if (u0 >= ue) break;
-    if (u1 <= u0 || u1 <= ua) continue;
-    const int seg = q - (int)(u0 / nwin);  // 0: the range starts in this panel block, 1: in the previous one
-    const int base = (int)((2 * b + seg) * kSkinnySlotBytes) + ((t * 4 + p) * 4 * 64 + lane) * 16;
+  for (int b0 = b_lo; b0 <= b_hi; b0 += kSkinnyBatch) {
+    f32x4 v[kSkinnyBatch][4];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-      acc[ct] += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prr, base + ct * 1024, 0, 0));
+    for (int c = 0; c < kSkinnyBatch; ++c) {
+      const int b = b0 + c;
+      const int off = b <= b_hi ? (int)((2 * b + (b == b_lo ? seg_lo : 0)) * kSkinnySlotBytes) + lo : kOOB;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        v[c][ct] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prr, off == kOOB ? kOOB : off + ct * 1024, 0, 0));
+    }
+#pragma unroll
+    for (int c = 0; c < kSkinnyBatch; ++c)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[ct] += v[c][ct];
   }
   epilogue(args, acc, panel, 16 * t, min(args.M, kSkinnyRows), lane);
 }
@@ -1211,16 +1245,17 @@ static void launch_dense_tiled(const GemmArgs& a, hipStream_t s) {
 int64_t gemm_partial_bytes() { return 2 * kSkinnyBlocks * kSkinnySlotBytes; }
 static bool skinny_ok(const GemmArgs& a) {
   return !a.offsets && a.a_fmt == A_BF16 && a.M <= kSkinnyRows && a.lda % 8 == 0 && a.K % 32 == 0 &&
-         a.partial && a.partial_bytes >= gemm_partial_bytes() && ceil_div(a.P, 4) <= kSkinnyBlocks &&
+         a.partial && a.partial_bytes >= gemm_partial_bytes() &&
+         ceil_div(a.P, 4) <= kSkinnyBlocks && ceil_div(a.P, 4) * a.wwin * (kSkinnyBlocks + 1) < ((int64_t)1 << 31) &&
          a.a_bytes < (int64_t)1 << 30 && (int64_t)a.P * a.wwin * kPanelWinBytes < (int64_t)1 << 30;
 }
 
 template <int TAG>
 static void launch_skinny(const GemmArgs& a, hipStream_t s) {
-  constexpr int DA = 2, DB = 4;
+  constexpr int DA = 2, NB = 3;  // deeper rings measured no faster
   const int nblk = (int)ceil_div(a.P, 4);
   const int G = (int)std::min<int64_t>(kSkinnyBlocks, (int64_t)nblk * a.wwin);  // nblk <= G <= windows
-  hipLaunchKernelGGL((skinny_gemm_kernel<DA, DB, TAG>), dim3(G), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((skinny_gemm_kernel<DA, NB, TAG>), dim3(G), dim3(512), 0, s, a);
   hipLaunchKernelGGL((skinny_reduce_kernel<TAG>), dim3(nblk, (unsigned)ceil_div(a.M, 16)), dim3(256), 0, s, a, G);
 }
 
