@@ -24,9 +24,9 @@ CALIB_BYTES = 1 << 30
 
 
 def stage_of(name: str):
-    if "panel_gemm_kernel" in name or "tiled_gemm_kernel" in name:
-        tag = int(name.split("(")[0].rstrip(">").split(",")[-1])
-        return STAGE[tag]
+    if any(k in name for k in ("panel_gemm_kernel", "tiled_gemm_kernel", "skinny_gemm_kernel", "skinny_reduce_kernel")):
+        tag = int(name.split(">(")[0].replace("<", ",").split(",")[-1])
+        return STAGE[tag] + (" (reduce)" if "skinny_reduce" in name else "")
     for s in ("topk", "route", "combine", "pack", "f32_to_bf16"):
         if s in name:
             return s

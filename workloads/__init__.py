@@ -223,6 +223,9 @@ WORKLOADS = {
                                         note="K3 shape decode, Zipf bias scaled to a 2-10x hot-expert load"),
     "k3_prefill_t8192": Workload("k3_prefill_t8192", LayerShape(**K3, act="mxfp8"), T=8192, seed=3,
                                  note="K3 shape prefill chunk, MXFP8 latent and hidden activations"),
+    "k3_t2048": Workload("k3_t2048", LayerShape(**K3), T=2048, seed=3,
+                         note="K3 shape, 2048 tokens, bf16 activations (the LatentMoE side of the "
+                              "full-width T = 2048 comparison)"),
     "fullwidth_t64": Workload("fullwidth_t64", LayerShape(d=7168, l=7168, h=3072, E=896, k=8, Ns=2, hs=3072,
                                                           latent_moe=0), T=64, seed=4,
                               note="conventional full-width MoE, top-8"),
