@@ -49,6 +49,19 @@ def recorded_traffic(workload: str, kernel: str):
     return None if k is None else k["hbm_bytes_per_launch"]
 
 
+def load_summary(counts):
+    """Per-expert token counts of one batch: the load histogram in brief."""
+    import numpy as np
+    c = np.sort(counts)[::-1]
+    act = c[c > 0]
+    return {"n_active": int(act.size), "mean": float(c.mean()), "max": int(c[0]),
+            "p50_active": float(np.percentile(act, 50)) if act.size else 0.0,
+            "p90_active": float(np.percentile(act, 90)) if act.size else 0.0,
+            "top8": [int(v) for v in c[:8]],
+            "hist_log2": {f"[{1 << b},{(1 << (b + 1)) - 1}]": int(((act >= (1 << b)) & (act < (1 << (b + 1)))).sum())
+                          for b in range(int(np.log2(max(int(c[0]), 1))) + 1)}}
+
+
 def mxfp4_bytes(n_elems: int) -> int:
     return n_elems // 2 + n_elems // 32
 
@@ -179,6 +192,8 @@ def main():
         "layer_mfma_frac": ideal_ms / ms_step,
         "active_experts": n_active,
         "max_over_mean_load": float(counts.max() / max(counts.mean(), 1e-9)),
+        "expert_load": load_summary(counts),
+        "dispatch_values_per_token": s.k * le,
         "stages_ms": stage_avg,
         "cpu_baseline": cpu,
     }

@@ -463,9 +463,17 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
   HIPCHECK(ctx, launch_route(idx, T, E, k, counts, offsets, perm, inv, (int32_t*)(ws + ctx->ws_route), s),
            "route launch");
   HIPCHECK(ctx, mark(ST_ROUTE, 1), "event");
-  // Experts averaging 32 or more rows use the LDS-tiled scaled-MFMA kernel (MXFP8 activations;
-  // its DMAs move whole 4-byte scale words, so both reduction widths must be multiples of 128)
-  const int many_rows = ((int64_t)T * k >= (int64_t)32 * E && le % 128 == 0 && h % 128 == 0) ? 1 : 0;
+  // Which experts take the row-tiled GEMMs (whole 128-wide K windows, so both reduction widths must be
+  // multiples of 128): with 32 or more rows per expert on average, all; with 8 or more, those with at
+  // least 32 rows (the panel kernel takes the rest: a skewed load puts hot experts on the tiled
+  // kernel); with fewer (decode), none.
+  int row_split = 0;
+  if (le % 128 == 0 && h % 128 == 0) {
+    if ((int64_t)T * k >= (int64_t)32 * E)
+      row_split = 1;
+    else if ((int64_t)T * k >= (int64_t)8 * E)
+      row_split = 32;
+  }
   // ---- gateup
   {
     GemmArgs a{};
@@ -491,7 +499,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     a.rowmap = perm;
     a.offsets = offsets;
     a.n_groups = E;
-    a.many_rows = many_rows;
+    a.row_split = row_split;
     EpiSeg& sg = a.seg[0];
     sg.p0 = 0;
     sg.p1 = ctx->gu_P;
@@ -527,7 +535,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     a.as_bytes = (int64_t)T * k * (h / 32);
     a.offsets = offsets;
     a.n_groups = E;
-    a.many_rows = many_rows;
+    a.row_split = row_split;
     EpiSeg& sg = a.seg[0];
     sg.p0 = 0;
     sg.p1 = ctx->dn_P;

@@ -96,7 +96,9 @@ struct GemmArgs {
   int32_t n_groups;        // grouped: number of groups
   int32_t M;               // dense: rows
   int32_t m_passes;        // dense: row passes (set by the launcher)
-  int32_t many_rows;       // grouped: rows per group large enough for the LDS-tiled scaled-MFMA kernel
+  int32_t row_split;       // grouped: 0 = the panel kernel takes every group; 1 = the row-tiled kernel takes
+                           // every group; n > 1 = groups of at least n rows take the row-tiled kernel and
+                           // the others the panel kernel (both launched; each skips the other's groups)
   int32_t nseg;
   EpiSeg seg[kMaxSeg];
   float* partial;          // dense launches of few rows: split-K partial sums (workspace), may be null

@@ -387,6 +387,7 @@ __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_ker
   const int ks = wave % KSPLIT;
   const bool panel_ok = panel < args.P;
   if (r0 >= r1 || pblock * BlockShape<KSPLIT>::panels >= args.P) return;  // uniform over the block
+  if (args.offsets && args.row_split > 1 && r1 - r0 >= args.row_split) return;  // the row-tiled kernel's group
 
   const int wbeg = (args.wwin * ks) / KSPLIT;
   const int wend = (args.wwin * (ks + 1)) / KSPLIT;
@@ -646,6 +647,7 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
   const int r0 = DENSE ? grp * ROWS : args.offsets[grp];
   const int r1 = DENSE ? min(r0 + ROWS, args.M) : args.offsets[grp + 1];
   if (r0 >= r1) return;  // uniform over the block
+  if (!DENSE && r1 - r0 < args.row_split) return;  // the panel kernel's group
   const int npan = min(4, args.P - panel0);
   const int nwin = args.wwin;
   // the block's (up to) four panels, one resource: panel p's window w at (p nwin + w) 4352
@@ -1203,13 +1205,17 @@ static void launch_one(GemmArgs a, hipStream_t s) {
                      0, s, a);
 }
 
-// The row-tiled kernel takes grouped MXFP8 launches with many rows per group, whole K windows,
-// 16-byte aligned activation rows, 4-byte aligned scale rows and one epilogue segment of the given
-// mode (GLU output rows 16-byte aligned, scale rows 4-byte aligned at panel-block granularity).
-static bool f8_grouped_ok(const GemmArgs& a, int mode) {
-  if (!a.many_rows || !a.offsets || a.a_fmt != A_MXFP8 || a.K % kWinK || a.lda % 16 || a.ldas % 4) return false;
+// Grouped launches split their groups by row count (row_split): the row-tiled kernel takes the groups
+// with many rows, the panel kernel the others. The row-tiled kernel needs whole K windows and 16-byte
+// aligned activation rows; MXFP8: 4-byte aligned scale rows and, for the GLU output, 16-byte aligned
+// output rows and scale rows 4-byte aligned at panel-block granularity. One epilogue segment of the
+// given mode covering every panel; activation offsets in 32 bits.
+static bool tiled_grouped_ok(const GemmArgs& a, int mode) {
+  if (a.row_split <= 0 || !a.offsets || a.K % kWinK || a.a_bytes >= ((int64_t)1 << 31) - (1 << 24)) return false;
   if (a.nseg != 1 || a.seg[0].p0 != 0 || a.seg[0].p1 < a.P || a.seg[0].mode != mode) return false;
   const EpiSeg& sg = a.seg[0];
+  if (a.a_fmt == A_BF16) return a.lda % 8 == 0;
+  if (a.a_fmt != A_MXFP8 || a.lda % 16 || a.ldas % 4) return false;
   if (mode == EPI_SWIGLU_MXFP8)
     return sg.ldo % 16 == 0 && sg.col0 % 128 == 0 && sg.ldos % 4 == 0 && sg.ncols == 32 * a.P;
   return true;
@@ -1221,6 +1227,16 @@ static void launch_f8(const GemmArgs& a, hipStream_t s) {
   const unsigned nblk = (unsigned)ceil_div(a.P, 4);
   const unsigned g8 = (unsigned)ceil_div(a.n_groups, 8) * 8;
   hipLaunchKernelGGL((tiled_gemm_kernel<A_MXFP8, false, DA, DB, MT, WPS, PPW, EPI, TAG>), dim3(g8 * nblk),
+                     dim3(256 * WPS), 0, s, a);
+}
+
+// bf16 grouped: 128-row chunks, the weights converted to bf16 operands once per window
+template <int EPI, int TAG>
+static void launch_bf16_grouped(const GemmArgs& a, hipStream_t s) {
+  constexpr int DA = 2, DB = 2, MT = 8, WPS = 2, PPW = 1;
+  const unsigned nblk = (unsigned)ceil_div(a.P, 4);
+  const unsigned g8 = (unsigned)ceil_div(a.n_groups, 8) * 8;
+  hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, false, DA, DB, MT, WPS, PPW, EPI, TAG>), dim3(g8 * nblk),
                      dim3(256 * WPS), 0, s, a);
 }
 
@@ -1280,21 +1296,34 @@ hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) 
         launch_one<8, A_BF16, 3, 1, true, GEMM_Y>(a, s);
       break;
     case GEMM_GATEUP:
-      if (a.a_fmt == A_BF16)
-        launch_one<1, A_BF16, 4, 1, true, GEMM_GATEUP>(a, s);  // weights 3 windows ahead
-      else if (f8_grouped_ok(a, EPI_SWIGLU_MXFP8))
-        launch_f8<1, GEMM_GATEUP>(a, s);
+    case GEMM_DOWN: {
+      const bool gu = stage == GEMM_GATEUP;
+      const bool bf = a.a_fmt == A_BF16;
+      const int mode = gu ? (bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_MXFP8) : EPI_F32;
+      GemmArgs pa = a;  // the panel kernel's share
+      if (tiled_grouped_ok(a, mode)) {
+        if (gu && bf)
+          launch_bf16_grouped<2, GEMM_GATEUP>(a, s);
+        else if (gu)
+          launch_f8<1, GEMM_GATEUP>(a, s);
+        else if (bf)
+          launch_bf16_grouped<0, GEMM_DOWN>(a, s);
+        else
+          launch_f8<0, GEMM_DOWN>(a, s);
+        if (a.row_split == 1) break;  // no group left for the panel kernel
+      } else {
+        pa.row_split = 0;
+      }
+      if (gu && bf)
+        launch_one<1, A_BF16, 4, 1, true, GEMM_GATEUP>(pa, s);  // weights 3 windows ahead
+      else if (gu)
+        launch_one<1, A_MXFP8, 3, 1, true, GEMM_GATEUP>(pa, s);
+      else if (bf)
+        launch_one<1, A_BF16, 3, 1, true, GEMM_DOWN>(pa, s);
       else
-        launch_one<1, A_MXFP8, 3, 1, true, GEMM_GATEUP>(a, s);
+        launch_one<1, A_MXFP8, 3, 1, true, GEMM_DOWN>(pa, s);
       break;
-    case GEMM_DOWN:
-      if (a.a_fmt == A_BF16)
-        launch_one<1, A_BF16, 3, 1, true, GEMM_DOWN>(a, s);
-      else if (f8_grouped_ok(a, EPI_F32))
-        launch_f8<0, GEMM_DOWN>(a, s);
-      else
-        launch_one<1, A_MXFP8, 3, 1, true, GEMM_DOWN>(a, s);
-      break;
+    }
     default:
       return hipErrorInvalidValue;
   }

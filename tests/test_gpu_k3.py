@@ -157,6 +157,12 @@ def test_k3_decode_repeat_bit_identical():
 
 
 @pytest.mark.timeout(900)
+def test_k3_t2048_bf16():
+    """K3 shape, 2048 tokens, bf16 activations: every expert on the row-tiled grouped bf16 kernel."""
+    check_layer(workloads.get("k3_t2048"), [0, 1000, 2047])
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("T", [64, 2048])
 def test_fullwidth(T):
     wl = workloads.get("fullwidth_t2048").with_tokens(T)

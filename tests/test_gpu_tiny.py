@@ -2,8 +2,9 @@
 
 Sizes: tiny LatentMoE (T = 64, d = 256, l = 128, hidden 96, E = 16, k = 4, one shared expert)
 and variants (MXFP8 activations, full-width conventional MoE, skewed bias with two shared
-experts, MXFP8 with many rows per expert over several K windows and row chunks); ragged token
-counts cover partial 16-row tiles and partial row chunks.
+experts, MXFP8 or bf16 with many rows per expert over several K windows and row chunks, a skewed
+load split between the row-tiled and the panel kernels); ragged token counts cover partial 16-row
+tiles and partial row chunks.
 """
 from __future__ import annotations
 
@@ -131,7 +132,8 @@ def check_all(name, T):
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_mxfp8", "tiny_mxfp8_many", "tiny_mxfp8_deep", "tiny_dense_many",
-                                  "tiny_fullwidth", "tiny_skewed"])
+                                  "tiny_fullwidth", "tiny_skewed", "tiny_bf16_many", "tiny_bf16_deep", "tiny_split",
+                                  "tiny_split_mxfp8"])
 def test_full_parity(name):
     check_all(name, workloads.get(name).T)
 
@@ -155,6 +157,27 @@ def test_mxfp8_many_rows_ragged(T):
 def test_mxfp8_deep_ragged(T):
     """Scaled-MFMA grouped kernel over several K windows and several 256-row chunks per expert."""
     check_all("tiny_mxfp8_deep", T)
+
+
+@pytest.mark.parametrize("T", [129, 333, 511])
+def test_bf16_many_rows_ragged(T):
+    """Row-tiled grouped bf16 kernel: expert row counts that leave partial 16-row tiles and chunks."""
+    check_all("tiny_bf16_many", T)
+
+
+@pytest.mark.parametrize("T", [1, 255, 777])
+def test_bf16_deep_ragged(T):
+    """Row-tiled grouped bf16 kernel over several K windows and several 128-row chunks per expert
+    (T = 1: the panel kernel alone)."""
+    check_all("tiny_bf16_deep", T)
+
+
+@pytest.mark.parametrize("name", ["tiny_split", "tiny_split_mxfp8"])
+@pytest.mark.parametrize("T", [63, 64, 100])
+def test_split_by_rows_ragged(name, T):
+    """8 to 32 rows per expert on average: experts with 32 or more rows on the row-tiled kernel, the
+    rest on the panel kernel, in the same stage (T = 63: the panel kernel alone)."""
+    check_all(name, T)
 
 
 @pytest.mark.parametrize("T", [1024, 1500])

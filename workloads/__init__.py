@@ -205,6 +205,19 @@ WORKLOADS = {
                                 zipf_alpha=0.2,
                                 note="tiny layer, MXFP8, several K windows, skewed rows per expert (some above "
                                      "256: several row chunks)"),
+    "tiny_bf16_many": Workload("tiny_bf16_many", LayerShape(d=256, l=128, h=128, E=16, k=4, Ns=1, hs=96), T=512,
+                               seed=0, note="tiny layer, bf16, 128 rows per expert (row-tiled grouped bf16 kernel)"),
+    "tiny_bf16_deep": Workload("tiny_bf16_deep", LayerShape(d=256, l=640, h=768, E=16, k=4, Ns=1, hs=64), T=1024,
+                               seed=7, bias="zipf", zipf_alpha=0.2,
+                               note="tiny layer, bf16, several K windows, skewed rows per expert (several "
+                                    "128-row chunks)"),
+    "tiny_split": Workload("tiny_split", LayerShape(d=256, l=128, h=128, E=16, k=2, Ns=1, hs=96), T=128, seed=9,
+                           bias="zipf", zipf_alpha=0.3,
+                           note="tiny layer, bf16, 16 rows per expert on average with a skewed load: experts "
+                                "of 32 or more rows on the row-tiled kernel, the others on the panel kernel"),
+    "tiny_split_mxfp8": Workload("tiny_split_mxfp8", LayerShape(d=256, l=128, h=128, E=16, k=2, Ns=1, hs=96,
+                                                                act="mxfp8"), T=128, seed=9, bias="zipf",
+                                 zipf_alpha=0.3, note="as tiny_split with MXFP8 latent and hidden activations"),
     "tiny_dense_many": Workload("tiny_dense_many", LayerShape(d=256, l=128, h=96, E=16, k=4, Ns=1, hs=96), T=2048,
                                 seed=8, note="tiny layer, bf16, 2048 tokens (row-tiled dense GEMMs, K tail "
                                              "in the latent/shared GEMM)"),
