@@ -465,14 +465,14 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
   HIPCHECK(ctx, mark(ST_ROUTE, 1), "event");
   // Which experts take the row-tiled GEMMs (whole 128-wide K windows, so both reduction widths must be
   // multiples of 128): with 32 or more rows per expert on average, all; with 8 or more, those with at
-  // least 32 rows (the panel kernel takes the rest: a skewed load puts hot experts on the tiled
-  // kernel); with fewer (decode), none.
+  // least 16 rows (the panel kernel, one pass per 16 rows, takes the rest: a skewed load puts hot
+  // experts on the tiled kernel); with fewer (decode), none.
   int row_split = 0;
   if (le % 128 == 0 && h % 128 == 0) {
     if ((int64_t)T * k >= (int64_t)32 * E)
       row_split = 1;
     else if ((int64_t)T * k >= (int64_t)8 * E)
-      row_split = 32;
+      row_split = 16;
   }
   // ---- gateup
   {

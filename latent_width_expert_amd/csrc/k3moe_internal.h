@@ -99,6 +99,8 @@ struct GemmArgs {
   int32_t row_split;       // grouped: 0 = the panel kernel takes every group; 1 = the row-tiled kernel takes
                            // every group; n > 1 = groups of at least n rows take the row-tiled kernel and
                            // the others the panel kernel (both launched; each skips the other's groups)
+  int32_t row_cap;         // grouped, row-tiled kernel: when > 0, groups of row_cap or more rows are left to
+                           // another row-tiled launch (set by the launcher)
   int32_t nseg;
   EpiSeg seg[kMaxSeg];
   float* partial;          // dense launches of few rows: split-K partial sums (workspace), may be null

@@ -647,7 +647,7 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
   const int r0 = DENSE ? grp * ROWS : args.offsets[grp];
   const int r1 = DENSE ? min(r0 + ROWS, args.M) : args.offsets[grp + 1];
   if (r0 >= r1) return;  // uniform over the block
-  if (!DENSE && r1 - r0 < args.row_split) return;  // the panel kernel's group
+  if (!DENSE && (r1 - r0 < args.row_split || (args.row_cap > 0 && r1 - r0 >= args.row_cap))) return;  // another launch's
   const int npan = min(4, args.P - panel0);
   const int nwin = args.wwin;
   // the block's (up to) four panels, one resource: panel p's window w at (p nwin + w) 4352
@@ -1230,14 +1230,24 @@ static void launch_f8(const GemmArgs& a, hipStream_t s) {
                      dim3(256 * WPS), 0, s, a);
 }
 
-// bf16 grouped: 128-row chunks, the weights converted to bf16 operands once per window
+// bf16 grouped, the weights converted to bf16 operands once per window. Experts below 64 rows: 64-row
+// chunks with the weights 4 windows ahead (with few rows the kernel is a weight stream and the depth
+// of the weight ring sets its rate); 64 rows or more: 128-row chunks, weights 2 windows ahead (the
+// activation stages take the room). Two launches, each skipping the other's experts.
+constexpr int kBf16SmallRows = 64;
 template <int EPI, int TAG>
 static void launch_bf16_grouped(const GemmArgs& a, hipStream_t s) {
-  constexpr int DA = 2, DB = 2, MT = 8, WPS = 2, PPW = 1;
+  constexpr int WPS = 2, PPW = 1;
   const unsigned nblk = (unsigned)ceil_div(a.P, 4);
   const unsigned g8 = (unsigned)ceil_div(a.n_groups, 8) * 8;
-  hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, false, DA, DB, MT, WPS, PPW, EPI, TAG>), dim3(g8 * nblk),
-                     dim3(256 * WPS), 0, s, a);
+  GemmArgs lo = a, hi = a;
+  lo.row_cap = kBf16SmallRows;
+  hi.row_split = std::max(a.row_split, kBf16SmallRows);
+  hi.row_cap = 0;
+  hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, false, 3, 4, 4, WPS, PPW, EPI, TAG>), dim3(g8 * nblk),
+                     dim3(256 * WPS), 0, s, lo);
+  hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, false, 2, 2, 8, WPS, PPW, EPI, TAG>), dim3(g8 * nblk),
+                     dim3(256 * WPS), 0, s, hi);
 }
 
 // Dense bf16 launches with enough rows to fill the chip with 128-row chunks (8 per XCD) take the
