@@ -638,11 +638,14 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int pg = wv % NPG, h = wv / NPG;        // panel group of the wave, its row-tile phase
   const int nblk = (args.P + 3) / 4;
-  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   // a group: an expert's rows (grouped) or a chunk of ROWS rows (dense, all on the same weights)
-  const int grp = xcd + 8 * (slot / nblk);
-  const int panel0 = 4 * (slot % nblk);
   const int ngrp = DENSE ? (args.M + ROWS - 1) / ROWS : args.n_groups;
+  // eight groups or more: group g on XCD g mod 8 (its panel blocks re-read its rows from that L2);
+  // fewer: the panel blocks of each group are dealt over all XCDs (block b: group b / nblk)
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const bool spread = ngrp < 8;
+  const int grp = spread ? (int)blockIdx.x / nblk : xcd + 8 * (slot / nblk);
+  const int panel0 = 4 * (spread ? (int)blockIdx.x % nblk : slot % nblk);
   if (grp >= ngrp) return;
   const int r0 = DENSE ? grp * ROWS : args.offsets[grp];
   const int r1 = DENSE ? min(r0 + ROWS, args.M) : args.offsets[grp + 1];
@@ -1250,20 +1253,28 @@ static void launch_bf16_grouped(const GemmArgs& a, hipStream_t s) {
                      dim3(256 * WPS), 0, s, hi);
 }
 
-// Dense bf16 launches with enough rows to fill the chip with 128-row chunks (8 per XCD) take the
-// row-tiled kernel; rows must be 16-byte aligned.
+// Dense bf16 launches (beyond the skinny kernel's rows) take the row-tiled kernel; rows must be 16-byte
+// aligned. With 1024 rows or more: 128-row chunks (at least 8, one XCD each); fewer: 64-row chunks
+// with the weights 4 windows ahead (few chunks: the kernel is mostly a weight stream).
 constexpr int kDenseRows = 128;
 static bool dense_tiled_ok(const GemmArgs& a) {
-  return !a.offsets && a.a_fmt == A_BF16 && a.M >= 8 * kDenseRows && a.lda % 8 == 0 && a.K % 32 == 0;
+  return !a.offsets && a.a_fmt == A_BF16 && a.M > 0 && a.lda % 8 == 0 && a.K % 32 == 0 &&
+         a.a_bytes < ((int64_t)1 << 31) - (1 << 24);
 }
 
 template <int TAG>
 static void launch_dense_tiled(const GemmArgs& a, hipStream_t s) {
-  constexpr int DA = 2, DB = 2, MT = kDenseRows / 16, WPS = 2, PPW = 1;
+  constexpr int WPS = 2, PPW = 1;
   const unsigned nblk = (unsigned)ceil_div(a.P, 4);
-  const unsigned g8 = (unsigned)ceil_div(ceil_div(a.M, kDenseRows), 8) * 8;
-  hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, true, DA, DB, MT, WPS, PPW, 2, TAG>), dim3(g8 * nblk), dim3(256 * WPS),
-                     0, s, a);
+  if (a.M >= 8 * kDenseRows) {
+    const unsigned g8 = (unsigned)ceil_div(ceil_div(a.M, kDenseRows), 8) * 8;
+    hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, true, 2, 2, kDenseRows / 16, WPS, PPW, 2, TAG>), dim3(g8 * nblk),
+                       dim3(256 * WPS), 0, s, a);
+  } else {
+    const unsigned g8 = (unsigned)ceil_div(ceil_div(a.M, 64), 8) * 8;
+    hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, true, 3, 4, 4, WPS, PPW, 2, TAG>), dim3(g8 * nblk), dim3(256 * WPS),
+                       0, s, a);
+  }
 }
 
 // Dense bf16 launches of at most 64 rows take the split-K skinny kernel when the workspace for its
