@@ -47,7 +47,9 @@ struct k3moe_ctx {
   size_t gu_stride = 0, dn_stride = 0;
   // workspace layout (for max_tokens)
   size_t ws_scores = 0, ws_idx = 0, ws_p = 0, ws_counts = 0, ws_offsets = 0, ws_perm = 0, ws_inv = 0, ws_route = 0;
-  size_t ws_z = 0, ws_zs = 0, ws_h = 0, ws_hs = 0, ws_o = 0, ws_abuf = 0, ws_u = 0, ws_partial = 0, ws_total = 0;
+  size_t ws_z = 0, ws_zs = 0, ws_h = 0, ws_hs = 0, ws_o = 0, ws_abuf = 0, ws_u = 0, ws_partial = 0, ws_items = 0;
+  size_t ws_total = 0;
+  bool use_items = false;  // grouped row-tiled launches walk a work-item list (persistent grid)
   // state
   uint8_t* packed = nullptr;
   bool dense_packed = false;
@@ -185,6 +187,9 @@ int k3moe_create(const k3moe_config* cfg, k3moe_ctx** out) {
   x->ws_abuf = take(2 * T * (size_t)x->y_K);
   x->ws_u = take(4 * T * le);
   x->ws_partial = take((size_t)gemm_partial_bytes());
+  const int nblk_max = (int)std::max(ceil_div(x->gu_P, 4), ceil_div(x->dn_P, 4));
+  x->use_items = tile_items_fit(c.max_tokens, E, nblk_max);
+  x->ws_items = take(x->use_items ? (size_t)tile_items_bytes((int64_t)T * k, E, nblk_max) : 0);
   x->ws_total = w;
   x->routed_packed.assign(E, 0);
   *out = x;
@@ -500,6 +505,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     a.offsets = offsets;
     a.n_groups = E;
     a.row_split = row_split;
+    a.items = ctx->use_items ? (int32_t*)(ws + ctx->ws_items) : nullptr;
     EpiSeg& sg = a.seg[0];
     sg.p0 = 0;
     sg.p1 = ctx->gu_P;
@@ -536,6 +542,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     a.offsets = offsets;
     a.n_groups = E;
     a.row_split = row_split;
+    a.items = ctx->use_items ? (int32_t*)(ws + ctx->ws_items) : nullptr;
     EpiSeg& sg = a.seg[0];
     sg.p0 = 0;
     sg.p1 = ctx->dn_P;

@@ -101,6 +101,8 @@ struct GemmArgs {
                            // the others the panel kernel (both launched; each skips the other's groups)
   int32_t row_cap;         // grouped, row-tiled kernel: when > 0, groups of row_cap or more rows are left to
                            // another row-tiled launch (set by the launcher)
+  int32_t* items;          // grouped, row-tiled kernel: workspace of tile_items_bytes() for the work-item
+                           // list (persistent grid); null: one block per (group, panel block)
   int32_t nseg;
   EpiSeg seg[kMaxSeg];
   float* partial;          // dense launches of few rows: split-K partial sums (workspace), may be null
@@ -114,6 +116,13 @@ hipError_t launch_pack(const PackJob& job, hipStream_t s);
 hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s);
 // workspace for the split-K partial sums of dense launches of at most 64 rows
 int64_t gemm_partial_bytes();
+// workspace for the work-item list of grouped row-tiled launches: a header of kItemHeader ints
+// (start of each XCD's list, then the total), then one int per item (expert | chunk << 12 |
+// panel block << 24) for up to max_rows rows over n_groups groups and at most nblk panel blocks
+// (chunks of at least 64 rows); tile_items_fit says whether the item format holds the launch
+constexpr int kItemHeader = 16;
+int64_t tile_items_bytes(int64_t max_rows, int n_groups, int nblk);
+bool tile_items_fit(int64_t max_rows_per_group, int n_groups, int nblk);
 hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int k, int32_t* idx, float* p,
                        hipStream_t s);
 // scratch: route_scratch_bytes(max_tokens, E) bytes of workspace (per-chunk expert counts); small T

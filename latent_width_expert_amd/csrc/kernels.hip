@@ -616,23 +616,25 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
   constexpr int RPD = 1024 / AROW;              // rows per 1 KB code DMA
   constexpr int ESZ = MX ? 1 : 2;               // bytes per activation element
   constexpr int A_SC = ROWS * AROW;
-  constexpr int A_STAGE = A_SC + (MX ? NWAVE * 256 : 0);  // MXFP8: one 256-byte scale slot per wave
+  constexpr int A_STAGE = A_SC + (MX ? ROWS * 4 : 0);  // MXFP8: 4 scale bytes per row (one word a K block)
   constexpr int B_STAGE = 4 * kPanelWinBytes;   // one panel-window per panel
   constexpr int APW = ROWS / RPD / NWAVE;       // 1 KB code DMAs per wave and window
   constexpr int AL = APW + (MX ? 1 : 0);        // + the wave's scale DMA
   constexpr int BPW = (20 + NWAVE - 1) / NWAVE; // the four panels' 5 weight DMAs each, over the waves
   constexpr int LPW = AL + BPW;
-  static_assert(4 % PPW == 0 && MT % NPH == 0 && (ROWS / RPD) % NWAVE == 0 && (!MX || ROWS <= 64 * NWAVE), "shape");
-  static_assert(DB >= DA && DA >= 1, "ring depths");
+  static_assert(4 % PPW == 0 && MT % NPH == 0 && (ROWS / RPD) % NWAVE == 0 && (!MX || (ROWS <= 64 * NWAVE && ROWS % 64 == 0)),
+                "shape");
+  static_assert(DA >= 1 && DB >= 1, "ring depths");
   // At step w the later of A(w) and B(w) must have landed. DB > DA: A(w) is the later one, followed
-  // by the B DMAs of its step and DA - 1 full steps; DB == DA: B(w) comes last in its step,
-  // followed by DA - 1 full steps.
-  constexpr int WAITN = (DB > DA ? BPW : 0) + (DA - 1) * LPW;
+  // by the B DMAs of its step and DA - 1 full steps; DB <= DA: B(w) comes last in its step,
+  // followed by DB - 1 full steps.
+  constexpr int WAITN = DB > DA ? BPW + (DA - 1) * LPW : (DB - 1) * LPW;
   static_assert(WAITN < 64, "vmcnt range");
   static_assert(EPI != 1 || (MX && ROWS * 132 <= A_STAGE), "epilogue staging fits one A stage");
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[NA][A_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[NB][B_STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_sink[NWAVE][256];
+  // target of placeholder DMAs (zeros or unused words, never read): one 256-byte row shared by the waves
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sink[256];
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -640,298 +642,322 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
   const int nblk = (args.P + 3) / 4;
   // a group: an expert's rows (grouped) or a chunk of ROWS rows (dense, all on the same weights)
   const int ngrp = DENSE ? (args.M + ROWS - 1) / ROWS : args.n_groups;
-  // eight groups or more: group g on XCD g mod 8 (its panel blocks re-read its rows from that L2);
-  // fewer: the panel blocks of each group are dealt over all XCDs (block b: group b / nblk)
-  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
-  const bool spread = ngrp < 8;
-  const int grp = spread ? (int)blockIdx.x / nblk : xcd + 8 * (slot / nblk);
-  const int panel0 = 4 * (spread ? (int)blockIdx.x % nblk : slot % nblk);
-  if (grp >= ngrp) return;
-  const int r0 = DENSE ? grp * ROWS : args.offsets[grp];
-  const int r1 = DENSE ? min(r0 + ROWS, args.M) : args.offsets[grp + 1];
-  if (r0 >= r1) return;  // uniform over the block
-  if (!DENSE && (r1 - r0 < args.row_split || (args.row_cap > 0 && r1 - r0 >= args.row_cap))) return;  // another launch's
-  const int npan = min(4, args.P - panel0);
-  const int nwin = args.wwin;
-  // the block's (up to) four panels, one resource: panel p's window w at (p nwin + w) 4352
-  const i32x4s wr = sgpr_rsrc(args.W + (DENSE ? 0 : (int64_t)grp * args.w_group_stride) +
-                                  (int64_t)panel0 * nwin * kPanelWinBytes,
-                              (int64_t)npan * nwin * kPanelWinBytes);
   const i32x4s ar = sgpr_rsrc(args.A, args.a_bytes);
   const i32x4s asr = sgpr_rsrc(args.A_scales, MX ? args.as_bytes : 0);
   const int g = lane >> 4, i16 = lane & 15;
   const u32 lds_a0 = lds_addr(&lds_a[0][0]), lds_b0 = lds_addr(&lds_b[0][0]);
-  const u32 lds_s = lds_addr(&lds_sink[wv][0]);
-
-  for (int mb = r0; mb < r1; mb += ROWS) {
-    // A DMAs of this wave: code instruction j = wv APW + jj covers chunk rows RPD j .. RPD j + RPD - 1
-    // (lane L: row RPD j + L / CPR, position L % CPR holding 16-byte chunk (L % CPR) ^ (row & 7) of
-    // the row's window); MXFP8: the scale instruction covers rows 64 wv .. 64 wv + 63 (lane L: row
-    // 64 wv + L). Rows past the chunk and elements past K read zeros.
-    int acode[APW], ascale = -1, akel[APW];
-#pragma unroll
-    for (int jj = 0; jj < APW; ++jj) {
-      const int row = mb + RPD * (wv * APW + jj) + lane / CPR;
-      acode[jj] = args.rowmap ? args.rowmap[min(row, r1 - 1)] : row;
-    }
-    if constexpr (MX) {
-      const int row = mb + 64 * wv + lane;
-      ascale = args.rowmap ? args.rowmap[min(row, r1 - 1)] : row;
-    }
-#pragma unroll
-    for (int jj = 0; jj < APW; ++jj) {
-      const int r = RPD * (wv * APW + jj) + lane / CPR;
-      const int c = (lane % CPR) ^ (r & 7);
-      akel[jj] = 16 * c / ESZ;  // first K element of the chunk inside the window
-      acode[jj] = mb + r < r1 ? acode[jj] * (int)args.lda * ESZ + 16 * c : -1;
-    }
-    if constexpr (MX) ascale = 64 * wv + lane < ROWS && mb + 64 * wv + lane < r1 ? ascale * (int)args.ldas : -1;
-    const u32 a_w = lds_a0 + 1024 * (wv * APW), a_s = lds_a0 + A_SC + 256 * wv;
-    // The LPW DMAs of step w, one by one: the wave's A code DMAs, its A scale DMA, then its share
-    // of the four panels' weight DMAs (items wv BPW .. wv BPW + BPW - 1 of: per panel four 1 KB code
-    // pieces and the 256-byte scale piece; items past 20 are 4-byte dummies into the wave's sink),
-    // always in this order so that one wait count holds at every step. Step w fills A stage
-    // (w + DA) % NA and B stage (w + DB) % NB; a stage index below zero in the prologue is a dummy.
-    auto issue_one = [&]<int d>(int w) {
-      if constexpr (d < AL) {
-        const int wa = w + DA;
-        const bool real = wa >= 0;
-        const bool in = real && wa < nwin;
-        const u32 st = (u32)((wa % NA) * A_STAGE);
-        if (!real)
-          dma4<false>(ar, lds_s, kOOB);  // prologue placeholder (4 bytes a lane: the sink holds 256)
-        else if constexpr (d < APW)
-          dma16<false>(ar, a_w + st + 1024 * d,
-                       in && acode[d] >= 0 && kWinK * wa + akel[d] < args.K ? acode[d] + AROW * wa : kOOB);
-        else
-          dma4<false>(asr, real ? a_s + st : lds_s, in && ascale >= 0 ? ascale + 4 * wa : kOOB);
-      } else {
-        const int wb = w + DB;
-        const int item = wv * BPW + (d - AL);  // uniform
-        const int p = item / 5, piece = item % 5;
-        const bool in = wb < nwin && p < npan;
-        const u32 st = lds_b0 + (u32)((wb % NB) * B_STAGE + p * kPanelWinBytes);
-        const int src = (p * nwin + wb) * kPanelWinBytes;
-        if (item >= 20)
-          dma4<false>(wr, lds_s, kOOB);
-        else if (piece < 4)
-          dma16<true>(wr, st + 1024 * piece, in ? src + 1024 * piece + lane * 16 : kOOB);
-        else
-          dma4<true>(wr, st + 4096, in ? src + 4096 + lane * 4 : kOOB);
-      }
-    };
-    auto issue_range = [&]<int D0, int D1>(int w) {
-      [&]<int... I>(std::integer_sequence<int, I...>) {
-        (issue_one.template operator()<D0 + I>(w), ...);
-      }(std::make_integer_sequence<int, D1 - D0>{});
-    };
-    // row tiles holding rows (uniform over the block) and this wave's share: tiles h, h + NPH, ...
-    const int nt = min(MT, (r1 - mb + 15) / 16);
-    const int nw = nt > h ? (nt - h + NPH - 1) / NPH : 0;
-
-    f32x4 acc[MTW][PPW][4];
-#pragma unroll
-    for (int j = 0; j < MTW; ++j)
-#pragma unroll
-      for (int pp = 0; pp < PPW; ++pp)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[j][pp][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // The window loop, specialised on the wave's number of row tiles holding rows (one variant per
-    // count, chosen once per chunk) so that each window's body is straight-line code.
-    auto run = [&]<int N>() {
-      // prologue: steps -DB .. -1 issue their DMAs in steady-state order
-      for (int i = -DB; i < 0; ++i) issue_range.template operator()<0, LPW>(i);
-      for (int w = 0; w < nwin; ++w) {
-        wait_vmcnt<WAITN>();
-        barrier_nowait();  // stages of w complete for every wave; stages of w - 1 free
-        // weights of the wave's panel-windows
-        u32x4 bw[PPW][4];
-        u32 bsc[PPW];
-#pragma unroll
-        for (int pp = 0; pp < PPW; ++pp) {
-          const uint8_t* sb = &lds_b[w % NB][(PPW * pg + pp) * kPanelWinBytes];
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) bw[pp][rt] = *(const u32x4*)(sb + rt * 1024 + lane * 16);
-          bsc[pp] = *(const u32*)(sb + 4096 + lane * 4);
-        }
-        // A operands: row tile t of the stage starts at t * 16 AROW (MXFP8 scales at A_SC + t * 64);
-        // the swizzle depends on the row only through row % 8 = i16 % 8. MXFP8 lane (i16, g): K bytes
-        // [16 g, +16) and [64 + 16 g, +16); bf16 lane (i16, g), step s: K elements [32 g + 8 s, +8).
-        const uint8_t* sa = lds_a[w % NA];
-        const uint8_t* prow = sa + i16 * AROW + h * 16 * AROW;
-        const uint8_t* psc = sa + A_SC + i16 * 4 + g + h * 64;
-        using ATileT = std::conditional_t<MX, i32x8, u32x4[4]>;
-        auto load_tile = [&](int j, ATileT& aop, int& asc) {  // the wave's j-th tile: row tile h + NPH j
-          const uint8_t* pr = prow + j * NPH * 16 * AROW;
-          if constexpr (MX) {
-            const u32x4 lo = *(const u32x4*)(pr + 16 * (g ^ (i16 & 7)));
-            const u32x4 hi = *(const u32x4*)(pr + 16 * ((4 + g) ^ (i16 & 7)));
-            asc = psc[j * NPH * 64];
-            aop = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          } else {
-#pragma unroll
-            for (int st = 0; st < 4; ++st) aop[st] = *(const u32x4*)(pr + 16 * ((4 * g + st) ^ (i16 & 7)));
-            asc = 0;
-          }
-        };
-        // bf16: the weights as bf16 MFMA operands, converted once per window
-        [[maybe_unused]] bf16x8 bcv[MX ? 1 : PPW][MX ? 1 : 4][MX ? 1 : 4];
-        if constexpr (!MX) {
-#pragma unroll
-          for (int pp = 0; pp < PPW; ++pp)
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-              for (int st = 0; st < 4; ++st)
-                bcv[pp][ct][st] = fp4_operand(bw[pp][ct][st], e8m0_f32((bsc[pp] >> (8 * ct)) & 0xFFu));
-        }
-        // the step's DMAs are spread over the tiles (the wave keeps the matrix core busy while the
-        // memory pipeline drains); the next tile's operands are read before each group of DMAs,
-        // which are compiler barriers for memory operations
-        if constexpr (N == 0) {
-          issue_range.template operator()<0, LPW>(w);
-        } else {
-          ATileT cur;
-          int csc;
-          load_tile(0, cur, csc);
-          [&]<int... JI>(std::integer_sequence<int, JI...>) {
-            ([&] {
-              constexpr int j = JI;
-              ATileT nxt;
-              int nsc = 0;
-              if constexpr (j + 1 < N) load_tile(j + 1, nxt, nsc);
-              if constexpr (MX) {
-#pragma unroll
-                for (int pp = 0; pp < PPW; ++pp)
-#pragma unroll
-                  for (int ct = 0; ct < 4; ++ct) {
-                    const i32x8 bop = {(int)bw[pp][ct][0], (int)bw[pp][ct][1], (int)bw[pp][ct][2], (int)bw[pp][ct][3],
-                                       0, 0, 0, 0};
-                    acc[j][pp][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        cur, bop, acc[j][pp][ct], 0, 4, 0, csc, 0, (int)(bsc[pp] >> (8 * ct)));
-                  }
-              } else {
-#pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                  const bf16x8 av = __builtin_bit_cast(bf16x8, cur[st]);
-#pragma unroll
-                  for (int pp = 0; pp < PPW; ++pp)
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct)
-                      acc[j][pp][ct] =
-                          __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bcv[pp][ct][st], acc[j][pp][ct], 0, 0, 0);
-                }
-              }
-              issue_range.template operator()<j * LPW / N, (j + 1) * LPW / N>(w);
-              if constexpr (j + 1 < N) {
-                if constexpr (MX) {
-                  cur = nxt;
-                } else {
-#pragma unroll
-                  for (int st = 0; st < 4; ++st) cur[st] = nxt[st];
-                }
-                csc = nsc;
-              }
-            }(), ...);
-          }(std::make_integer_sequence<int, N>{});
-        }
-      }
-    };
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      ((nw == I ? (run.template operator()<I>(), 0) : 0), ...);
-    }(std::make_integer_sequence<int, MTW + 1>{});
-    wait_vmcnt<0>();
-    __syncthreads();  // rings idle
-
-    // epilogue; lane indices re-derived (opaque to the compiler) so that no address arithmetic is
-    // hoisted out of the chunk loop
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int eg = ln >> 4, ej = ln & 15;
-    const EpiSeg& sg = args.seg[0];
-    const int nrow = min(ROWS, r1 - mb);
-    if constexpr (EPI == 1) {
-      // codes staged as [ROWS][128 bytes] (32 units per panel), scales as [ROWS][4]
-      uint8_t* stg = &lds_a[0][0];
-      uint8_t* stg_sc = stg + ROWS * 128;
-      const bool tap = sg.pre != nullptr;
-      const rsrc_t prr = make_rsrc(tap ? sg.pre + (int64_t)mb * sg.ldpre : nullptr,
-                                   tap ? (int64_t)nrow * sg.ldpre * 4 : 0);
-#pragma unroll
-      for (int j = 0; j < MTW; ++j) {
-#pragma unroll
-        for (int pp = 0; pp < PPW; ++pp) {
-          const int pl = PPW * pg + pp;  // panel inside the block
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float v0 = silu(acc[j][pp][0][r]) * acc[j][pp][1][r];
-            const float v1 = silu(acc[j][pp][2][r]) * acc[j][pp][3][r];
-            const int lr = 16 * (h + NPH * j) + 4 * eg + r;
-            if (tap) {
-              const int o = lr * (int)sg.ldpre + sg.col0 + 32 * (panel0 + pl) + ej;
-              const bool ok = lr < nrow && pl < npan;
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), prr, ok ? 4 * o : kOOB, 0, 0);
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), prr, ok ? 4 * (o + 16) : kOOB, 0, 0);
-            }
-            u32 c0, c1, sb;
-            mxfp8_block(v0, v1, c0, c1, sb);
-            stg[lr * 128 + 32 * pl + ej] = (uint8_t)c0;
-            stg[lr * 128 + 32 * pl + 16 + ej] = (uint8_t)c1;
-            stg_sc[lr * 4 + pl] = (uint8_t)sb;  // the 16 lanes of the block agree
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __syncthreads();
-      const int t = threadIdx.x;
-      uint8_t* out = (uint8_t*)sg.out + sg.col0 + 32 * panel0;
-#pragma unroll
-      for (int q = 0; q < ROWS / (32 * WPS); ++q) {
-        const int lr = 32 * WPS * q + t / 8, piece = t % 8;
-        if (lr < nrow && piece < 2 * npan)
-          *(u32x4*)(out + (int64_t)(mb + lr) * sg.ldo + 16 * piece) = *(const u32x4*)(stg + lr * 128 + 16 * piece);
-      }
-      for (int lr = t; lr < nrow; lr += 256 * WPS) {
-        uint8_t* os = sg.out_scales + (int64_t)(mb + lr) * sg.ldos + sg.col0 / 32 + panel0;
-        if (npan == 4)
-          *(u32*)os = *(const u32*)(stg_sc + 4 * lr);
-        else
-          for (int p = 0; p < npan; ++p) os[p] = stg_sc[4 * lr + p];
-      }
-    } else if constexpr (EPI == 2) {
-      // per-panel segment modes (sigmoid, bf16, MX encode, SwiGLU, bf16 + addend)
-#pragma unroll
-      for (int pp = 0; pp < PPW; ++pp) {
-        if (PPW * pg + pp < npan) {
-#pragma unroll
-          for (int j = 0; j < MTW; ++j)
-            if (16 * (h + NPH * j) < nrow)
-              epilogue(args, acc[j][pp], panel0 + PPW * pg + pp, mb + 16 * (h + NPH * j), r1, ln);
-        }
-      }
+  const u32 lds_s = lds_addr(&lds_sink[0]);
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  // Work units. Grouped launches with an item list: a persistent grid (a multiple of 8 blocks) whose
+  // blocks walk the list of their XCD, one item (expert, chunk of ROWS rows, panel block) at a time
+  // (tile_items_kernel; the experts of XCD x are those with e mod 8 = x, so their rows are re-read
+  // from that L2). Otherwise one block per (group, panel block): eight groups or more, group g on
+  // XCD g mod 8; fewer, the panel blocks of each group dealt over all XCDs (block b: group b / nblk).
+  const bool listed = !DENSE && args.items != nullptr;
+  int it = 0, it_end = 1, it_step = 1;
+  if (listed) {
+    it = args.items[xcd] + slot;
+    it_end = args.items[xcd + 1];
+    it_step = (int)gridDim.x / 8;
+  }
+  for (; it < it_end; it += it_step) {
+    int grp, panel0, r0, r1;
+    if (listed) {
+      const u32 item = (u32)args.items[kItemHeader + it];
+      grp = (int)(item & 0xFFFu);
+      panel0 = 4 * (int)(item >> 24);
+      r0 = args.offsets[grp] + ROWS * (int)((item >> 12) & 0xFFFu);
+      r1 = min(r0 + ROWS, args.offsets[grp + 1]);
     } else {
-      const rsrc_t orr = make_rsrc((float*)sg.out + (int64_t)mb * sg.ldo + sg.col0, (int64_t)nrow * sg.ldo * 4);
-#pragma unroll
-      for (int j = 0; j < MTW; ++j) {
-#pragma unroll
-        for (int pp = 0; pp < PPW; ++pp) {
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct) {
-            const int pl = PPW * pg + pp;
-            const int col = 64 * (panel0 + pl) + 16 * ct + ej;
-#pragma unroll
+      const bool spread = ngrp < 8;
+      grp = spread ? (int)blockIdx.x / nblk : xcd + 8 * (slot / nblk);
+      panel0 = 4 * (spread ? (int)blockIdx.x % nblk : slot % nblk);
+      if (grp >= ngrp) return;
+      r0 = DENSE ? grp * ROWS : args.offsets[grp];
+      r1 = DENSE ? min(r0 + ROWS, args.M) : args.offsets[grp + 1];
+      if (r0 >= r1) return;  // uniform over the block
+      // a group of another launch (the panel kernel's, or the other row band's)
+      if (!DENSE && (r1 - r0 < args.row_split || (args.row_cap > 0 && r1 - r0 >= args.row_cap))) return;
+    }
+    const int npan = min(4, args.P - panel0);
+    const int nwin = args.wwin;
+    // the block's (up to) four panels, one resource: panel p's window w at (p nwin + w) 4352
+    const i32x4s wr = sgpr_rsrc(args.W + (DENSE ? 0 : (int64_t)grp * args.w_group_stride) +
+                                    (int64_t)panel0 * nwin * kPanelWinBytes,
+                                (int64_t)npan * nwin * kPanelWinBytes);
+
+    for (int mb = r0; mb < r1; mb += ROWS) {
+      // A DMAs of this wave: code instruction j = wv APW + jj covers chunk rows RPD j .. RPD j + RPD - 1
+      // (lane L: row RPD j + L / CPR, position L % CPR holding 16-byte chunk (L % CPR) ^ (row & 7) of
+      // the row's window); MXFP8: the scale instruction covers rows 64 wv .. 64 wv + 63 (lane L: row
+      // 64 wv + L; waves past the chunk's rows send theirs to the sink). Rows past the chunk and
+      // elements past K read zeros.
+      int acode[APW], ascale = -1, akel[APW];
+  #pragma unroll
+      for (int jj = 0; jj < APW; ++jj) {
+        const int row = mb + RPD * (wv * APW + jj) + lane / CPR;
+        acode[jj] = args.rowmap ? args.rowmap[min(row, r1 - 1)] : row;
+      }
+      if constexpr (MX) {
+        const int row = mb + 64 * wv + lane;
+        ascale = args.rowmap ? args.rowmap[min(row, r1 - 1)] : row;
+      }
+  #pragma unroll
+      for (int jj = 0; jj < APW; ++jj) {
+        const int r = RPD * (wv * APW + jj) + lane / CPR;
+        const int c = (lane % CPR) ^ (r & 7);
+        akel[jj] = 16 * c / ESZ;  // first K element of the chunk inside the window
+        acode[jj] = mb + r < r1 ? acode[jj] * (int)args.lda * ESZ + 16 * c : -1;
+      }
+      if constexpr (MX) ascale = 64 * wv + lane < ROWS && mb + 64 * wv + lane < r1 ? ascale * (int)args.ldas : -1;
+      const u32 a_w = lds_a0 + 1024 * (wv * APW), a_s = lds_a0 + A_SC + 256 * wv;
+      // The LPW DMAs of step w, one by one: the wave's A code DMAs, its A scale DMA, then its share
+      // of the four panels' weight DMAs (items wv BPW .. wv BPW + BPW - 1 of: per panel four 1 KB code
+      // pieces and the 256-byte scale piece; items past 20 are 4-byte dummies into the sink),
+      // always in this order so that one wait count holds at every step. Step w fills A stage
+      // (w + DA) % NA and B stage (w + DB) % NB; a window index below zero (prologue) is a dummy.
+      auto issue_one = [&]<int d>(int w) {
+        if constexpr (d < AL) {
+          const int wa = w + DA;
+          const bool real = wa >= 0;
+          const bool in = real && wa < nwin;
+          const u32 st = (u32)((wa % NA) * A_STAGE);
+          if (!real)
+            dma4<false>(ar, lds_s, kOOB);  // prologue placeholder (4 bytes a lane: the sink holds 256)
+          else if constexpr (d < APW)
+            dma16<false>(ar, a_w + st + 1024 * d,
+                         in && acode[d] >= 0 && kWinK * wa + akel[d] < args.K ? acode[d] + AROW * wa : kOOB);
+          else
+            dma4<false>(asr, 64 * wv < ROWS ? a_s + st : lds_s, in && ascale >= 0 ? ascale + 4 * wa : kOOB);
+        } else {
+          const int wb = w + DB;
+          const bool real = wb >= 0;
+          const int item = wv * BPW + (d - AL);  // uniform
+          const int p = item / 5, piece = item % 5;
+          const bool in = wb < nwin && p < npan;
+          const u32 st = lds_b0 + (u32)(((real ? wb : 0) % NB) * B_STAGE + p * kPanelWinBytes);
+          const int src = (p * nwin + wb) * kPanelWinBytes;
+          if (item >= 20 || !real)
+            dma4<false>(wr, lds_s, kOOB);
+          else if (piece < 4)
+            dma16<true>(wr, st + 1024 * piece, in ? src + 1024 * piece + lane * 16 : kOOB);
+          else
+            dma4<true>(wr, st + 4096, in ? src + 4096 + lane * 4 : kOOB);
+        }
+      };
+      auto issue_range = [&]<int D0, int D1>(int w) {
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+          (issue_one.template operator()<D0 + I>(w), ...);
+        }(std::make_integer_sequence<int, D1 - D0>{});
+      };
+      // row tiles holding rows (uniform over the block) and this wave's share: tiles h, h + NPH, ...
+      const int nt = min(MT, (r1 - mb + 15) / 16);
+      const int nw = nt > h ? (nt - h + NPH - 1) / NPH : 0;
+
+      f32x4 acc[MTW][PPW][4];
+  #pragma unroll
+      for (int j = 0; j < MTW; ++j)
+  #pragma unroll
+        for (int pp = 0; pp < PPW; ++pp)
+  #pragma unroll
+          for (int ct = 0; ct < 4; ++ct) acc[j][pp][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+      // The window loop, specialised on the wave's number of row tiles holding rows (one variant per
+      // count, chosen once per chunk) so that each window's body is straight-line code.
+      auto run = [&]<int N>() {
+        // prologue: steps -max(DA, DB) .. -1 issue their DMAs in steady-state order
+        for (int i = -(DA > DB ? DA : DB); i < 0; ++i) issue_range.template operator()<0, LPW>(i);
+        for (int w = 0; w < nwin; ++w) {
+          wait_vmcnt<WAITN>();
+          barrier_nowait();  // stages of w complete for every wave; stages of w - 1 free
+          // weights of the wave's panel-windows
+          u32x4 bw[PPW][4];
+          u32 bsc[PPW];
+  #pragma unroll
+          for (int pp = 0; pp < PPW; ++pp) {
+            const uint8_t* sb = &lds_b[w % NB][(PPW * pg + pp) * kPanelWinBytes];
+  #pragma unroll
+            for (int rt = 0; rt < 4; ++rt) bw[pp][rt] = *(const u32x4*)(sb + rt * 1024 + lane * 16);
+            bsc[pp] = *(const u32*)(sb + 4096 + lane * 4);
+          }
+          // A operands: row tile t of the stage starts at t * 16 AROW (MXFP8 scales at A_SC + t * 64);
+          // the swizzle depends on the row only through row % 8 = i16 % 8. MXFP8 lane (i16, g): K bytes
+          // [16 g, +16) and [64 + 16 g, +16); bf16 lane (i16, g), step s: K elements [32 g + 8 s, +8).
+          const uint8_t* sa = lds_a[w % NA];
+          const uint8_t* prow = sa + i16 * AROW + h * 16 * AROW;
+          const uint8_t* psc = sa + A_SC + i16 * 4 + g + h * 64;
+          using ATileT = std::conditional_t<MX, i32x8, u32x4[4]>;
+          auto load_tile = [&](int j, ATileT& aop, int& asc) {  // the wave's j-th tile: row tile h + NPH j
+            const uint8_t* pr = prow + j * NPH * 16 * AROW;
+            if constexpr (MX) {
+              const u32x4 lo = *(const u32x4*)(pr + 16 * (g ^ (i16 & 7)));
+              const u32x4 hi = *(const u32x4*)(pr + 16 * ((4 + g) ^ (i16 & 7)));
+              asc = psc[j * NPH * 64];
+              aop = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            } else {
+  #pragma unroll
+              for (int st = 0; st < 4; ++st) aop[st] = *(const u32x4*)(pr + 16 * ((4 * g + st) ^ (i16 & 7)));
+              asc = 0;
+            }
+          };
+          // bf16: the weights as bf16 MFMA operands, converted once per window
+          [[maybe_unused]] bf16x8 bcv[MX ? 1 : PPW][MX ? 1 : 4][MX ? 1 : 4];
+          if constexpr (!MX) {
+  #pragma unroll
+            for (int pp = 0; pp < PPW; ++pp)
+  #pragma unroll
+              for (int ct = 0; ct < 4; ++ct)
+  #pragma unroll
+                for (int st = 0; st < 4; ++st)
+                  bcv[pp][ct][st] = fp4_operand(bw[pp][ct][st], e8m0_f32((bsc[pp] >> (8 * ct)) & 0xFFu));
+          }
+          // the step's DMAs are spread over the tiles (the wave keeps the matrix core busy while the
+          // memory pipeline drains); the next tile's operands are read before each group of DMAs,
+          // which are compiler barriers for memory operations
+          if constexpr (N == 0) {
+            issue_range.template operator()<0, LPW>(w);
+          } else {
+            ATileT cur;
+            int csc;
+            load_tile(0, cur, csc);
+            [&]<int... JI>(std::integer_sequence<int, JI...>) {
+              ([&] {
+                constexpr int j = JI;
+                ATileT nxt;
+                int nsc = 0;
+                if constexpr (j + 1 < N) load_tile(j + 1, nxt, nsc);
+                if constexpr (MX) {
+  #pragma unroll
+                  for (int pp = 0; pp < PPW; ++pp)
+  #pragma unroll
+                    for (int ct = 0; ct < 4; ++ct) {
+                      const i32x8 bop = {(int)bw[pp][ct][0], (int)bw[pp][ct][1], (int)bw[pp][ct][2], (int)bw[pp][ct][3],
+                                         0, 0, 0, 0};
+                      acc[j][pp][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                          cur, bop, acc[j][pp][ct], 0, 4, 0, csc, 0, (int)(bsc[pp] >> (8 * ct)));
+                    }
+                } else {
+  #pragma unroll
+                  for (int st = 0; st < 4; ++st) {
+                    const bf16x8 av = __builtin_bit_cast(bf16x8, cur[st]);
+  #pragma unroll
+                    for (int pp = 0; pp < PPW; ++pp)
+  #pragma unroll
+                      for (int ct = 0; ct < 4; ++ct)
+                        acc[j][pp][ct] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bcv[pp][ct][st], acc[j][pp][ct], 0, 0, 0);
+                  }
+                }
+                issue_range.template operator()<j * LPW / N, (j + 1) * LPW / N>(w);
+                if constexpr (j + 1 < N) {
+                  if constexpr (MX) {
+                    cur = nxt;
+                  } else {
+  #pragma unroll
+                    for (int st = 0; st < 4; ++st) cur[st] = nxt[st];
+                  }
+                  csc = nsc;
+                }
+              }(), ...);
+            }(std::make_integer_sequence<int, N>{});
+          }
+        }
+      };
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((nw == I ? (run.template operator()<I>(), 0) : 0), ...);
+      }(std::make_integer_sequence<int, MTW + 1>{});
+      wait_vmcnt<0>();
+      __syncthreads();  // rings idle
+
+      // epilogue; lane indices re-derived (opaque to the compiler) so that no address arithmetic is
+      // hoisted out of the chunk loop
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int eg = ln >> 4, ej = ln & 15;
+      const EpiSeg& sg = args.seg[0];
+      const int nrow = min(ROWS, r1 - mb);
+      if constexpr (EPI == 1) {
+        // codes staged as [ROWS][128 bytes] (32 units per panel), scales as [ROWS][4]
+        uint8_t* stg = &lds_a[0][0];
+        uint8_t* stg_sc = stg + ROWS * 128;
+        const bool tap = sg.pre != nullptr;
+        const rsrc_t prr = make_rsrc(tap ? sg.pre + (int64_t)mb * sg.ldpre : nullptr,
+                                     tap ? (int64_t)nrow * sg.ldpre * 4 : 0);
+  #pragma unroll
+        for (int j = 0; j < MTW; ++j) {
+  #pragma unroll
+          for (int pp = 0; pp < PPW; ++pp) {
+            const int pl = PPW * pg + pp;  // panel inside the block
+  #pragma unroll
             for (int r = 0; r < 4; ++r) {
+              const float v0 = silu(acc[j][pp][0][r]) * acc[j][pp][1][r];
+              const float v1 = silu(acc[j][pp][2][r]) * acc[j][pp][3][r];
               const int lr = 16 * (h + NPH * j) + 4 * eg + r;
-              const bool ok = lr < nrow && pl < npan && col < sg.ncols;
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][pp][ct][r]), orr,
-                                                    ok ? 4 * (lr * (int)sg.ldo + col) : kOOB, 0, 0);
+              if (tap) {
+                const int o = lr * (int)sg.ldpre + sg.col0 + 32 * (panel0 + pl) + ej;
+                const bool ok = lr < nrow && pl < npan;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), prr, ok ? 4 * o : kOOB, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), prr, ok ? 4 * (o + 16) : kOOB, 0, 0);
+              }
+              u32 c0, c1, sb;
+              mxfp8_block(v0, v1, c0, c1, sb);
+              stg[lr * 128 + 32 * pl + ej] = (uint8_t)c0;
+              stg[lr * 128 + 32 * pl + 16 + ej] = (uint8_t)c1;
+              stg_sc[lr * 4 + pl] = (uint8_t)sb;  // the 16 lanes of the block agree
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        const int t = threadIdx.x;
+        uint8_t* out = (uint8_t*)sg.out + sg.col0 + 32 * panel0;
+  #pragma unroll
+        for (int q = 0; q < ROWS / (32 * WPS); ++q) {
+          const int lr = 32 * WPS * q + t / 8, piece = t % 8;
+          if (lr < nrow && piece < 2 * npan)
+            *(u32x4*)(out + (int64_t)(mb + lr) * sg.ldo + 16 * piece) = *(const u32x4*)(stg + lr * 128 + 16 * piece);
+        }
+        for (int lr = t; lr < nrow; lr += 256 * WPS) {
+          uint8_t* os = sg.out_scales + (int64_t)(mb + lr) * sg.ldos + sg.col0 / 32 + panel0;
+          if (npan == 4)
+            *(u32*)os = *(const u32*)(stg_sc + 4 * lr);
+          else
+            for (int p = 0; p < npan; ++p) os[p] = stg_sc[4 * lr + p];
+        }
+      } else if constexpr (EPI == 2) {
+        // per-panel segment modes (sigmoid, bf16, MX encode, SwiGLU, bf16 + addend)
+  #pragma unroll
+        for (int pp = 0; pp < PPW; ++pp) {
+          if (PPW * pg + pp < npan) {
+  #pragma unroll
+            for (int j = 0; j < MTW; ++j)
+              if (16 * (h + NPH * j) < nrow)
+                epilogue(args, acc[j][pp], panel0 + PPW * pg + pp, mb + 16 * (h + NPH * j), r1, ln);
+          }
+        }
+      } else {
+        const rsrc_t orr = make_rsrc((float*)sg.out + (int64_t)mb * sg.ldo + sg.col0, (int64_t)nrow * sg.ldo * 4);
+  #pragma unroll
+        for (int j = 0; j < MTW; ++j) {
+  #pragma unroll
+          for (int pp = 0; pp < PPW; ++pp) {
+  #pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+              const int pl = PPW * pg + pp;
+              const int col = 64 * (panel0 + pl) + 16 * ct + ej;
+  #pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int lr = 16 * (h + NPH * j) + 4 * eg + r;
+                const bool ok = lr < nrow && pl < npan && col < sg.ncols;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][pp][ct][r]), orr,
+                                                      ok ? 4 * (lr * (int)sg.ldo + col) : kOOB, 0, 0);
+              }
             }
           }
         }
       }
+      __syncthreads();  // staging and rings are reused by the next chunk
     }
-    __syncthreads();  // staging and rings are reused by the next chunk
   }
 }
 
@@ -1224,13 +1250,79 @@ static bool tiled_grouped_ok(const GemmArgs& a, int mode) {
   return true;
 }
 
+// Work-item list of a grouped row-tiled launch (one block of 1024 threads): the experts taken in XCD
+// classes (class x: experts x, x + 8, ...), each contributing ceil(rows / ROWS) chunks x nblk panel
+// blocks if its row count is in [max(split, 1), cap) (cap 0: unbounded), in the order (expert,
+// chunk, panel block); out[x] = start of class x's items, out[8] = the total.
+constexpr int kMinChunkRows = 64;
+int64_t tile_items_bytes(int64_t max_rows, int n_groups, int nblk) {
+  return 4 * (kItemHeader + (int64_t)nblk * (n_groups + max_rows / kMinChunkRows + 1));
+}
+bool tile_items_fit(int64_t max_rows_per_group, int n_groups, int nblk) {
+  return n_groups >= 1 && n_groups <= 2048 && nblk >= 1 && nblk <= 256 && max_rows_per_group / kMinChunkRows < 4095;
+}
+
+__device__ __forceinline__ int tile_items_of(const int32_t* offsets, int E, int per, int q, int split, int cap,
+                                             int rows, int nblk, int& e, int& nch) {
+  e = 8 * (q % per) + q / per;
+  nch = 0;
+  if (q >= 8 * per || e >= E) return 0;
+  const int c = offsets[e + 1] - offsets[e];
+  if (c < max(split, 1) || (cap > 0 && c >= cap)) return 0;
+  nch = (c + rows - 1) / rows;
+  return nch * nblk;
+}
+
+__global__ __launch_bounds__(1024) void tile_items_kernel(const int32_t* __restrict__ offsets, int E, int split, int cap,
+                                                          int rows, int nblk, int32_t* __restrict__ out) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int per = (E + 7) / 8;             // experts per XCD class
+  const int qpt = (8 * per + 1023) / 1024; // class positions per thread (q = x per + i: expert 8 i + x)
+  int sum = 0, e, nch;
+  for (int j = 0; j < qpt; ++j) sum += tile_items_of(offsets, E, per, t * qpt + j, split, cap, rows, nblk, e, nch);
+  part[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan over the threads
+    const int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int base = part[t] - sum;
+  for (int j = 0; j < qpt; ++j) {
+    const int q = t * qpt + j;
+    const int n = tile_items_of(offsets, E, per, q, split, cap, rows, nblk, e, nch);
+    if (q < 8 * per && q % per == 0) out[q / per] = base;
+    for (int ck = 0; ck < nch; ++ck)
+      for (int pb = 0; pb < nblk; ++pb)
+        out[kItemHeader + base + ck * nblk + pb] = (int32_t)((u32)e | ((u32)ck << 12) | ((u32)pb << 24));
+    base += n;
+  }
+  if (t == 1023) out[8] = part[1023];
+}
+
+// A grouped row-tiled launch: with an item list, the list for this row band and chunk height, then
+// a persistent grid of one block per CU; without, one block per (group, panel block).
+constexpr int kItemGrid = 256;
+template <int DA, int DB, int MT, int EPI, int TAG, int AF>
+static void launch_grouped_tiled(const GemmArgs& a, hipStream_t s) {
+  constexpr int WPS = 2, PPW = 1;
+  const unsigned nblk = (unsigned)ceil_div(a.P, 4);
+  unsigned grid = (unsigned)ceil_div(a.n_groups, 8) * 8 * nblk;
+  if (a.items) {
+    hipLaunchKernelGGL(tile_items_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.n_groups, a.row_split, a.row_cap,
+                       16 * MT, (int)nblk, a.items);
+    grid = kItemGrid;
+  }
+  hipLaunchKernelGGL((tiled_gemm_kernel<AF, false, DA, DB, MT, WPS, PPW, EPI, TAG>), dim3(grid), dim3(256 * WPS), 0,
+                     s, a);
+}
+
 template <int EPI, int TAG>
 static void launch_f8(const GemmArgs& a, hipStream_t s) {
-  constexpr int DA = 2, DB = 3, MT = 12, WPS = 2, PPW = 1;
-  const unsigned nblk = (unsigned)ceil_div(a.P, 4);
-  const unsigned g8 = (unsigned)ceil_div(a.n_groups, 8) * 8;
-  hipLaunchKernelGGL((tiled_gemm_kernel<A_MXFP8, false, DA, DB, MT, WPS, PPW, EPI, TAG>), dim3(g8 * nblk),
-                     dim3(256 * WPS), 0, s, a);
+  // 192-row chunks; activation rows 3 windows ahead, weights 2
+  launch_grouped_tiled<3, 2, 12, EPI, TAG, A_MXFP8>(a, s);
 }
 
 // bf16 grouped, the weights converted to bf16 operands once per window. Experts below 64 rows: 64-row
@@ -1240,17 +1332,12 @@ static void launch_f8(const GemmArgs& a, hipStream_t s) {
 constexpr int kBf16SmallRows = 64;
 template <int EPI, int TAG>
 static void launch_bf16_grouped(const GemmArgs& a, hipStream_t s) {
-  constexpr int WPS = 2, PPW = 1;
-  const unsigned nblk = (unsigned)ceil_div(a.P, 4);
-  const unsigned g8 = (unsigned)ceil_div(a.n_groups, 8) * 8;
   GemmArgs lo = a, hi = a;
   lo.row_cap = kBf16SmallRows;
   hi.row_split = std::max(a.row_split, kBf16SmallRows);
   hi.row_cap = 0;
-  hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, false, 3, 4, 4, WPS, PPW, EPI, TAG>), dim3(g8 * nblk),
-                     dim3(256 * WPS), 0, s, lo);
-  hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, false, 2, 2, 8, WPS, PPW, EPI, TAG>), dim3(g8 * nblk),
-                     dim3(256 * WPS), 0, s, hi);
+  launch_grouped_tiled<3, 4, 4, EPI, TAG, A_BF16>(lo, s);
+  launch_grouped_tiled<2, 2, 8, EPI, TAG, A_BF16>(hi, s);
 }
 
 // Dense bf16 launches (beyond the skinny kernel's rows) take the row-tiled kernel; rows must be 16-byte
