@@ -27,6 +27,8 @@ def stage_of(name: str):
     if any(k in name for k in ("panel_gemm_kernel", "tiled_gemm_kernel", "skinny_gemm_kernel", "skinny_reduce_kernel")):
         tag = int(name.split(">(")[0].replace("<", ",").split(",")[-1])
         return STAGE[tag] + (" (reduce)" if "skinny_reduce" in name else "")
+    if "tile_items" in name:
+        return "gateup/down (item list)"
     for s in ("topk", "route", "combine", "pack", "f32_to_bf16"):
         if s in name:
             return s
