@@ -133,7 +133,7 @@ def check_all(name, T):
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_mxfp8", "tiny_mxfp8_many", "tiny_mxfp8_deep", "tiny_dense_many",
                                   "tiny_fullwidth", "tiny_skewed", "tiny_bf16_many", "tiny_bf16_deep", "tiny_split",
-                                  "tiny_split_mxfp8"])
+                                  "tiny_split_mxfp8", "tiny_e12_mxfp8", "tiny_e4_bf16"])
 def test_full_parity(name):
     check_all(name, workloads.get(name).T)
 

@@ -218,6 +218,11 @@ WORKLOADS = {
     "tiny_split_mxfp8": Workload("tiny_split_mxfp8", LayerShape(d=256, l=128, h=128, E=16, k=2, Ns=1, hs=96,
                                                                 act="mxfp8"), T=128, seed=9, bias="zipf",
                                  zipf_alpha=0.3, note="as tiny_split with MXFP8 latent and hidden activations"),
+    "tiny_e12_mxfp8": Workload("tiny_e12_mxfp8", LayerShape(d=256, l=128, h=128, E=12, k=3, Ns=1, hs=96,
+                                                            act="mxfp8"), T=512, seed=10,
+                               note="tiny layer, MXFP8, 12 experts (XCD classes of unequal size), many rows"),
+    "tiny_e4_bf16": Workload("tiny_e4_bf16", LayerShape(d=256, l=128, h=128, E=4, k=2, Ns=1, hs=96), T=256,
+                             seed=11, note="tiny layer, bf16, 4 experts (XCD classes without experts), many rows"),
     "tiny_dense_many": Workload("tiny_dense_many", LayerShape(d=256, l=128, h=96, E=16, k=4, Ns=1, hs=96), T=2048,
                                 seed=8, note="tiny layer, bf16, 2048 tokens (row-tiled dense GEMMs, K tail "
                                              "in the latent/shared GEMM)"),
