@@ -925,16 +925,16 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
             for (int p = 0; p < npan; ++p) os[p] = stg_sc[4 * lr + p];
         }
       } else if constexpr (EPI == 2) {
-        // per-panel segment modes (sigmoid, bf16, MX encode, SwiGLU, bf16 + addend)
-  #pragma unroll
-        for (int pp = 0; pp < PPW; ++pp) {
-          if (PPW * pg + pp < npan) {
-  #pragma unroll
-            for (int j = 0; j < MTW; ++j)
-              if (16 * (h + NPH * j) < nrow)
-                epilogue(args, acc[j][pp], panel0 + PPW * pg + pp, mb + 16 * (h + NPH * j), r1, ln);
-          }
-        }
+        // per-panel segment modes (sigmoid, bf16, MX encode, SwiGLU, bf16 + addend); tile and panel
+        // indices are compile-time (a fold, not a loop the compiler may keep rolled), so the
+        // accumulators stay in registers instead of being copied to scratch for dynamic indexing
+        [&]<int... JP>(std::integer_sequence<int, JP...>) {
+          ([&] {
+            constexpr int j = JP / PPW, pp = JP % PPW;
+            if (PPW * pg + pp < npan && 16 * (h + NPH * j) < nrow)
+              epilogue(args, acc[j][pp], panel0 + PPW * pg + pp, mb + 16 * (h + NPH * j), r1, ln);
+          }(), ...);
+        }(std::make_integer_sequence<int, MTW * PPW>{});
       } else {
         const rsrc_t orr = make_rsrc((float*)sg.out + (int64_t)mb * sg.ldo + sg.col0, (int64_t)nrow * sg.ldo * 4);
   #pragma unroll
