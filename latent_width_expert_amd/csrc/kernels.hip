@@ -523,8 +523,17 @@ __device__ __forceinline__ i32x4s sgpr_rsrc(const void* base, int64_t bytes) {
 __device__ __forceinline__ u32 lds_addr(const void* p) {
   return (u32)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
+// The DMA operands that must sit in scalar registers (the buffer resource and the LDS address, which
+// are uniform over the wave by construction) pass through readfirstlane, a no-op for values the
+// compiler already keeps scalar and a guarantee where it cannot prove them uniform.
+__device__ __forceinline__ i32x4s sgpr4(i32x4s r) {
+  return i32x4s{__builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
+                __builtin_amdgcn_readfirstlane(r.z), __builtin_amdgcn_readfirstlane(r.w)};
+}
 template <bool NT>
 __device__ __forceinline__ void dma16(i32x4s r, u32 lds, int voff) {
+  r = sgpr4(r);
+  lds = __builtin_amdgcn_readfirstlane(lds);
   int m0save;
   if constexpr (NT)
     asm volatile(
@@ -549,6 +558,8 @@ __device__ __forceinline__ void dma16(i32x4s r, u32 lds, int voff) {
 }
 template <bool NT>
 __device__ __forceinline__ void dma4(i32x4s r, u32 lds, int voff) {
+  r = sgpr4(r);
+  lds = __builtin_amdgcn_readfirstlane(lds);
   int m0save;
   if constexpr (NT)
     asm volatile(
@@ -654,45 +665,61 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
   // from that L2). Otherwise one block per (group, panel block): eight groups or more, group g on
   // XCD g mod 8; fewer, the panel blocks of each group dealt over all XCDs (block b: group b / nblk).
   const bool listed = !DENSE && args.items != nullptr;
-  int it = 0, it_end = 1, it_step = 1;
+  int it = 0, it_end = 0, it_step = 1;
+  int cgrp = 0, cpanel0 = 0, cmb = 0, cr1 = 0;  // without a list: the block's group and its next chunk
   if (listed) {
     it = args.items[xcd] + slot;
     it_end = args.items[xcd + 1];
     it_step = (int)gridDim.x / 8;
+  } else {
+    const bool spread = ngrp < 8;
+    cgrp = spread ? (int)blockIdx.x / nblk : xcd + 8 * (slot / nblk);
+    cpanel0 = 4 * (spread ? (int)blockIdx.x % nblk : slot % nblk);
+    if (cgrp >= ngrp) return;
+    cmb = DENSE ? cgrp * ROWS : args.offsets[cgrp];
+    cr1 = DENSE ? min(cmb + ROWS, args.M) : args.offsets[cgrp + 1];
+    if (cmb >= cr1) return;  // uniform over the block
+    // a group of another launch (the panel kernel's, or the other row band's)
+    if (!DENSE && (cr1 - cmb < args.row_split || (args.row_cap > 0 && cr1 - cmb >= args.row_cap))) return;
   }
-  for (; it < it_end; it += it_step) {
-    int grp, panel0, r0, r1;
+  const int nwin = args.wwin;
+  const u32 a_w = lds_a0 + 1024 * (wv * APW), a_s = lds_a0 + A_SC + 256 * wv;
+  // The unit in hand: rows [mb, min(mb + ROWS, r1)) of group grp (a listed item, or the next chunk of
+  // the block's group) on panels panel0 .. panel0 + npan - 1, and the sources of its DMAs.
+  int grp = 0, panel0 = 0, mb = 0, r1 = 0, npan = 0;
+  i32x4s wr = {};
+  int acode[APW], ascale = -1, akel[APW];
+  auto next_unit = [&]() __attribute__((always_inline)) -> bool {
     if (listed) {
+      if (it >= it_end) return false;
       const u32 item = (u32)args.items[kItemHeader + it];
+      it += it_step;
       grp = (int)(item & 0xFFFu);
       panel0 = 4 * (int)(item >> 24);
-      r0 = args.offsets[grp] + ROWS * (int)((item >> 12) & 0xFFFu);
-      r1 = min(r0 + ROWS, args.offsets[grp + 1]);
+      mb = args.offsets[grp] + ROWS * (int)((item >> 12) & 0xFFFu);
+      r1 = min(mb + ROWS, args.offsets[grp + 1]);
     } else {
-      const bool spread = ngrp < 8;
-      grp = spread ? (int)blockIdx.x / nblk : xcd + 8 * (slot / nblk);
-      panel0 = 4 * (spread ? (int)blockIdx.x % nblk : slot % nblk);
-      if (grp >= ngrp) return;
-      r0 = DENSE ? grp * ROWS : args.offsets[grp];
-      r1 = DENSE ? min(r0 + ROWS, args.M) : args.offsets[grp + 1];
-      if (r0 >= r1) return;  // uniform over the block
-      // a group of another launch (the panel kernel's, or the other row band's)
-      if (!DENSE && (r1 - r0 < args.row_split || (args.row_cap > 0 && r1 - r0 >= args.row_cap))) return;
+      if (cmb >= cr1) return false;
+      grp = cgrp;
+      panel0 = cpanel0;
+      mb = cmb;
+      r1 = cr1;
+      cmb += ROWS;
     }
-    const int npan = min(4, args.P - panel0);
-    const int nwin = args.wwin;
-    // the block's (up to) four panels, one resource: panel p's window w at (p nwin + w) 4352
-    const i32x4s wr = sgpr_rsrc(args.W + (DENSE ? 0 : (int64_t)grp * args.w_group_stride) +
-                                    (int64_t)panel0 * nwin * kPanelWinBytes,
-                                (int64_t)npan * nwin * kPanelWinBytes);
-
-    for (int mb = r0; mb < r1; mb += ROWS) {
+    // uniform over the block: kept in scalar registers across units
+    grp = __builtin_amdgcn_readfirstlane(grp);
+    panel0 = __builtin_amdgcn_readfirstlane(panel0);
+    mb = __builtin_amdgcn_readfirstlane(mb);
+    r1 = __builtin_amdgcn_readfirstlane(r1);
+    npan = min(4, args.P - panel0);
+    // the unit's (up to) four panels, one resource: panel p's window w at (p nwin + w) 4352
+    wr = sgpr_rsrc(args.W + (DENSE ? 0 : (int64_t)grp * args.w_group_stride) + (int64_t)panel0 * nwin * kPanelWinBytes,
+                   (int64_t)npan * nwin * kPanelWinBytes);
       // A DMAs of this wave: code instruction j = wv APW + jj covers chunk rows RPD j .. RPD j + RPD - 1
       // (lane L: row RPD j + L / CPR, position L % CPR holding 16-byte chunk (L % CPR) ^ (row & 7) of
       // the row's window); MXFP8: the scale instruction covers rows 64 wv .. 64 wv + 63 (lane L: row
       // 64 wv + L; waves past the chunk's rows send theirs to the sink). Rows past the chunk and
       // elements past K read zeros.
-      int acode[APW], ascale = -1, akel[APW];
   #pragma unroll
       for (int jj = 0; jj < APW; ++jj) {
         const int row = mb + RPD * (wv * APW + jj) + lane / CPR;
@@ -710,7 +737,8 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
         acode[jj] = mb + r < r1 ? acode[jj] * (int)args.lda * ESZ + 16 * c : -1;
       }
       if constexpr (MX) ascale = 64 * wv + lane < ROWS && mb + 64 * wv + lane < r1 ? ascale * (int)args.ldas : -1;
-      const u32 a_w = lds_a0 + 1024 * (wv * APW), a_s = lds_a0 + A_SC + 256 * wv;
+    return true;
+  };
       // The LPW DMAs of step w, one by one: the wave's A code DMAs, its A scale DMA, then its share
       // of the four panels' weight DMAs (items wv BPW .. wv BPW + BPW - 1 of: per panel four 1 KB code
       // pieces and the 256-byte scale piece; items past 20 are 4-byte dummies into the sink),
@@ -750,11 +778,108 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
           (issue_one.template operator()<D0 + I>(w), ...);
         }(std::make_integer_sequence<int, D1 - D0>{});
       };
+  auto prologue = [&]() __attribute__((always_inline)) {  // steps -max(DA, DB) .. -1, in steady-state order
+    for (int i = -(DA > DB ? DA : DB); i < 0; ++i) issue_range.template operator()<0, LPW>(i);
+  };
+  f32x4 acc[MTW][PPW][4];
+  // the epilogue of a unit (its rows, group end and panels given; the accumulators as they stand)
+  auto finish = [&](const int mb, const int r1, const int panel0, const int npan) __attribute__((always_inline)) {
+      // epilogue; lane indices re-derived (opaque to the compiler) so that no address arithmetic is
+      // hoisted out of the chunk loop
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int eg = ln >> 4, ej = ln & 15;
+      const EpiSeg& sg = args.seg[0];
+      const int nrow = min(ROWS, r1 - mb);
+      if constexpr (EPI == 1) {
+        // codes staged as [ROWS][128 bytes] (32 units per panel), scales as [ROWS][4]
+        uint8_t* stg = &lds_a[NA - 1][0];  // A stage NA - 1: no prologue DMA writes it
+        uint8_t* stg_sc = stg + ROWS * 128;
+        const bool tap = sg.pre != nullptr;
+        const rsrc_t prr = make_rsrc(tap ? sg.pre + (int64_t)mb * sg.ldpre : nullptr,
+                                     tap ? (int64_t)nrow * sg.ldpre * 4 : 0);
+  #pragma unroll
+        for (int j = 0; j < MTW; ++j) {
+  #pragma unroll
+          for (int pp = 0; pp < PPW; ++pp) {
+            const int pl = PPW * pg + pp;  // panel inside the block
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float v0 = silu(acc[j][pp][0][r]) * acc[j][pp][1][r];
+              const float v1 = silu(acc[j][pp][2][r]) * acc[j][pp][3][r];
+              const int lr = 16 * (h + NPH * j) + 4 * eg + r;
+              if (tap) {
+                const int o = lr * (int)sg.ldpre + sg.col0 + 32 * (panel0 + pl) + ej;
+                const bool ok = lr < nrow && pl < npan;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), prr, ok ? 4 * o : kOOB, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), prr, ok ? 4 * (o + 16) : kOOB, 0, 0);
+              }
+              u32 c0, c1, sb;
+              mxfp8_block(v0, v1, c0, c1, sb);
+              stg[lr * 128 + 32 * pl + ej] = (uint8_t)c0;
+              stg[lr * 128 + 32 * pl + 16 + ej] = (uint8_t)c1;
+              stg_sc[lr * 4 + pl] = (uint8_t)sb;  // the 16 lanes of the block agree
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        const int t = threadIdx.x;
+        uint8_t* out = (uint8_t*)sg.out + sg.col0 + 32 * panel0;
+  #pragma unroll
+        for (int q = 0; q < ROWS / (32 * WPS); ++q) {
+          const int lr = 32 * WPS * q + t / 8, piece = t % 8;
+          if (lr < nrow && piece < 2 * npan)
+            *(u32x4*)(out + (int64_t)(mb + lr) * sg.ldo + 16 * piece) = *(const u32x4*)(stg + lr * 128 + 16 * piece);
+        }
+        for (int lr = t; lr < nrow; lr += 256 * WPS) {
+          uint8_t* os = sg.out_scales + (int64_t)(mb + lr) * sg.ldos + sg.col0 / 32 + panel0;
+          if (npan == 4)
+            *(u32*)os = *(const u32*)(stg_sc + 4 * lr);
+          else
+            for (int p = 0; p < npan; ++p) os[p] = stg_sc[4 * lr + p];
+        }
+      } else if constexpr (EPI == 2) {
+        // per-panel segment modes (sigmoid, bf16, MX encode, SwiGLU, bf16 + addend); tile and panel
+        // indices are compile-time (a fold, not a loop the compiler may keep rolled), so the
+        // accumulators stay in registers instead of being copied to scratch for dynamic indexing
+        [&]<int... JP>(std::integer_sequence<int, JP...>) {
+          ([&] {
+            constexpr int j = JP / PPW, pp = JP % PPW;
+            if (PPW * pg + pp < npan && 16 * (h + NPH * j) < nrow)
+              epilogue(args, acc[j][pp], panel0 + PPW * pg + pp, mb + 16 * (h + NPH * j), r1, ln);
+          }(), ...);
+        }(std::make_integer_sequence<int, MTW * PPW>{});
+      } else {
+        const rsrc_t orr = make_rsrc((float*)sg.out + (int64_t)mb * sg.ldo + sg.col0, (int64_t)nrow * sg.ldo * 4);
+  #pragma unroll
+        for (int j = 0; j < MTW; ++j) {
+  #pragma unroll
+          for (int pp = 0; pp < PPW; ++pp) {
+  #pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+              const int pl = PPW * pg + pp;
+              const int col = 64 * (panel0 + pl) + 16 * ct + ej;
+  #pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int lr = 16 * (h + NPH * j) + 4 * eg + r;
+                const bool ok = lr < nrow && pl < npan && col < sg.ncols;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][pp][ct][r]), orr,
+                                                      ok ? 4 * (lr * (int)sg.ldo + col) : kOOB, 0, 0);
+              }
+            }
+          }
+        }
+      }
+  };
+
+  bool have = next_unit();
+  if (have) prologue();
+  while (have) {
       // row tiles holding rows (uniform over the block) and this wave's share: tiles h, h + NPH, ...
       const int nt = min(MT, (r1 - mb + 15) / 16);
       const int nw = nt > h ? (nt - h + NPH - 1) / NPH : 0;
 
-      f32x4 acc[MTW][PPW][4];
   #pragma unroll
       for (int j = 0; j < MTW; ++j)
   #pragma unroll
@@ -765,8 +890,6 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
       // The window loop, specialised on the wave's number of row tiles holding rows (one variant per
       // count, chosen once per chunk) so that each window's body is straight-line code.
       auto run = [&]<int N>() {
-        // prologue: steps -max(DA, DB) .. -1 issue their DMAs in steady-state order
-        for (int i = -(DA > DB ? DA : DB); i < 0; ++i) issue_range.template operator()<0, LPW>(i);
         for (int w = 0; w < nwin; ++w) {
           wait_vmcnt<WAITN>();
           barrier_nowait();  // stages of w complete for every wave; stages of w - 1 free
@@ -868,96 +991,15 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
       }(std::make_integer_sequence<int, MTW + 1>{});
       wait_vmcnt<0>();
       __syncthreads();  // rings idle
-
-      // epilogue; lane indices re-derived (opaque to the compiler) so that no address arithmetic is
-      // hoisted out of the chunk loop
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int eg = ln >> 4, ej = ln & 15;
-      const EpiSeg& sg = args.seg[0];
-      const int nrow = min(ROWS, r1 - mb);
-      if constexpr (EPI == 1) {
-        // codes staged as [ROWS][128 bytes] (32 units per panel), scales as [ROWS][4]
-        uint8_t* stg = &lds_a[0][0];
-        uint8_t* stg_sc = stg + ROWS * 128;
-        const bool tap = sg.pre != nullptr;
-        const rsrc_t prr = make_rsrc(tap ? sg.pre + (int64_t)mb * sg.ldpre : nullptr,
-                                     tap ? (int64_t)nrow * sg.ldpre * 4 : 0);
-  #pragma unroll
-        for (int j = 0; j < MTW; ++j) {
-  #pragma unroll
-          for (int pp = 0; pp < PPW; ++pp) {
-            const int pl = PPW * pg + pp;  // panel inside the block
-  #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float v0 = silu(acc[j][pp][0][r]) * acc[j][pp][1][r];
-              const float v1 = silu(acc[j][pp][2][r]) * acc[j][pp][3][r];
-              const int lr = 16 * (h + NPH * j) + 4 * eg + r;
-              if (tap) {
-                const int o = lr * (int)sg.ldpre + sg.col0 + 32 * (panel0 + pl) + ej;
-                const bool ok = lr < nrow && pl < npan;
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), prr, ok ? 4 * o : kOOB, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), prr, ok ? 4 * (o + 16) : kOOB, 0, 0);
-              }
-              u32 c0, c1, sb;
-              mxfp8_block(v0, v1, c0, c1, sb);
-              stg[lr * 128 + 32 * pl + ej] = (uint8_t)c0;
-              stg[lr * 128 + 32 * pl + 16 + ej] = (uint8_t)c1;
-              stg_sc[lr * 4 + pl] = (uint8_t)sb;  // the 16 lanes of the block agree
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        __syncthreads();
-        const int t = threadIdx.x;
-        uint8_t* out = (uint8_t*)sg.out + sg.col0 + 32 * panel0;
-  #pragma unroll
-        for (int q = 0; q < ROWS / (32 * WPS); ++q) {
-          const int lr = 32 * WPS * q + t / 8, piece = t % 8;
-          if (lr < nrow && piece < 2 * npan)
-            *(u32x4*)(out + (int64_t)(mb + lr) * sg.ldo + 16 * piece) = *(const u32x4*)(stg + lr * 128 + 16 * piece);
-        }
-        for (int lr = t; lr < nrow; lr += 256 * WPS) {
-          uint8_t* os = sg.out_scales + (int64_t)(mb + lr) * sg.ldos + sg.col0 / 32 + panel0;
-          if (npan == 4)
-            *(u32*)os = *(const u32*)(stg_sc + 4 * lr);
-          else
-            for (int p = 0; p < npan; ++p) os[p] = stg_sc[4 * lr + p];
-        }
-      } else if constexpr (EPI == 2) {
-        // per-panel segment modes (sigmoid, bf16, MX encode, SwiGLU, bf16 + addend); tile and panel
-        // indices are compile-time (a fold, not a loop the compiler may keep rolled), so the
-        // accumulators stay in registers instead of being copied to scratch for dynamic indexing
-        [&]<int... JP>(std::integer_sequence<int, JP...>) {
-          ([&] {
-            constexpr int j = JP / PPW, pp = JP % PPW;
-            if (PPW * pg + pp < npan && 16 * (h + NPH * j) < nrow)
-              epilogue(args, acc[j][pp], panel0 + PPW * pg + pp, mb + 16 * (h + NPH * j), r1, ln);
-          }(), ...);
-        }(std::make_integer_sequence<int, MTW * PPW>{});
-      } else {
-        const rsrc_t orr = make_rsrc((float*)sg.out + (int64_t)mb * sg.ldo + sg.col0, (int64_t)nrow * sg.ldo * 4);
-  #pragma unroll
-        for (int j = 0; j < MTW; ++j) {
-  #pragma unroll
-          for (int pp = 0; pp < PPW; ++pp) {
-  #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-              const int pl = PPW * pg + pp;
-              const int col = 64 * (panel0 + pl) + 16 * ct + ej;
-  #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int lr = 16 * (h + NPH * j) + 4 * eg + r;
-                const bool ok = lr < nrow && pl < npan && col < sg.ncols;
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][pp][ct][r]), orr,
-                                                      ok ? 4 * (lr * (int)sg.ldo + col) : kOOB, 0, 0);
-              }
-            }
-          }
-        }
-      }
-      __syncthreads();  // staging and rings are reused by the next chunk
-    }
+      // The next unit's prologue DMAs go out before this unit's epilogue (into A stages 0 .. DA - 1 and
+      // the B stages; the epilogue stages in A stage NA - 1), so the memory path keeps working while
+      // the epilogue computes; the full drain below holds whatever order loads and stores finish in.
+      const int e_mb = mb, e_r1 = r1, e_panel0 = panel0, e_npan = npan;
+      have = next_unit();
+      if (have) prologue();
+      finish(e_mb, e_r1, e_panel0, e_npan);
+      wait_vmcnt<0>();
+      __syncthreads();  // staging and rings are reused by the next unit
   }
 }
 
