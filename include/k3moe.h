@@ -109,7 +109,7 @@ typedef struct {
 
 /*
  * Optional copies of intermediate results (device pointers; NULL = not captured), written by
- * k3moe_forward_ex on the stream during or after the forward. Row order of h, h_f32 and expert_out is the
+ * k3moe_forward_ex on the stream after the forward. Row order of h, h_f32 and expert_out is the
  * dispatched (expert-contiguous) order; inv maps (t, j) to that row.
  *   scores     fp32 [T, E]      s = Sigmoid(W_r x)
  *   topk_idx   int32 [T, k]     selected experts, descending s + b, ties to the lower id
@@ -124,9 +124,7 @@ typedef struct {
  *   h          [T*k, hidden]    GLU hidden after quantisation: bf16, or E4M3 codes
  *   h_scales   uint8 [T*k, hidden/32]
  *   h_f32      fp32 [T*k, hidden]  GLU hidden before quantisation
- *   expert_out fp32 [T*k, le]   routed expert outputs in fp32 (the combine reads them as fp32, or
- *                                rounded to bf16 when few rows per expert leave them all to the
- *                                panel kernel)
+ *   expert_out fp32 [T*k, le]   routed expert outputs
  *   u          fp32 [T, le]     p-weighted combine (eq. 11)
  *   n          bf16 [T, l]      RMSNorm(u) (latent_moe only)
  *   hs         bf16 [T, n_shared * shared_hidden]  shared GLU hiddens, expert-major columns

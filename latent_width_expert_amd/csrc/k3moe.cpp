@@ -183,7 +183,7 @@ int k3moe_create(const k3moe_config* cfg, k3moe_ctx** out) {
   }
   x->ws_h = take((f8 ? 1 : 2) * T * k * h);
   x->ws_hs = take(f8 ? T * k * h / 32 : 0);
-  x->ws_o = take(4 * T * k * le);  // expert outputs O: fp32, or bf16 in the first half
+  x->ws_o = take(4 * T * k * le);
   x->ws_abuf = take(2 * T * (size_t)x->y_K);
   x->ws_u = take(4 * T * le);
   x->ws_partial = take((size_t)gemm_partial_bytes());
@@ -394,7 +394,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
   uint8_t* zs = ws + ctx->ws_zs;
   uint8_t* H = ws + ctx->ws_h;
   uint8_t* Hs = ws + ctx->ws_hs;
-  void* O = ws + ctx->ws_o;
+  float* O = (float*)(ws + ctx->ws_o);
   uint16_t* abuf = (uint16_t*)(ws + ctx->ws_abuf);
   float* u = (float*)(ws + ctx->ws_u);
   const uint8_t* P = ctx->packed;
@@ -479,7 +479,6 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     else if ((int64_t)T * k >= (int64_t)8 * E)
       row_split = 16;
   }
-  const bool o_bf16 = row_split == 0;  // expert outputs stored in bf16 (see the down stage)
   // ---- gateup
   {
     GemmArgs a{};
@@ -547,18 +546,10 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     EpiSeg& sg = a.seg[0];
     sg.p0 = 0;
     sg.p1 = ctx->dn_P;
-    // O in bf16 when the panel kernel takes every expert (few rows: its stores are a small share of the
-    // stream, and the combine reads half the bytes); in fp32 when the row-tiled kernel runs, whose
-    // direct fp32 stores are cheaper than its bf16 segment epilogue. The fp32 values are tapped
-    // before any rounding.
-    sg.mode = o_bf16 ? EPI_BF16 : EPI_F32;
+    sg.mode = EPI_F32;
     sg.ncols = le;
     sg.out = O;
     sg.ldo = le;
-    if (taps && taps->expert_out && o_bf16) {
-      sg.pre = taps->expert_out;
-      sg.ldpre = le;
-    }
     a.nseg = 1;
     HIPCHECK(ctx, mark(ST_DOWN, 0), "event");
     HIPCHECK(ctx, launch_panel_gemm(a, GEMM_DOWN, s), "down launch");
@@ -568,11 +559,10 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
   HIPCHECK(ctx, mark(ST_COMBINE, 0), "event");
   if (c.latent_moe) {
     HIPCHECK(ctx,
-             launch_combine(O, o_bf16, inv, p, T, k, le, gamma, c.rms_eps, 0, abuf, ctx->y_K, taps ? taps->u : nullptr,
-                            s),
+             launch_combine(O, inv, p, T, k, le, gamma, c.rms_eps, 0, abuf, ctx->y_K, taps ? taps->u : nullptr, s),
              "combine launch");
   } else {
-    HIPCHECK(ctx, launch_combine(O, o_bf16, inv, p, T, k, le, nullptr, 0.0f, 1, nullptr, 0, u, s), "combine launch");
+    HIPCHECK(ctx, launch_combine(O, inv, p, T, k, le, nullptr, 0.0f, 1, nullptr, 0, u, s), "combine launch");
   }
   HIPCHECK(ctx, mark(ST_COMBINE, 1), "event");
   // ---- y_gemm
@@ -626,7 +616,7 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
     }
     HIPCHECK(ctx, cp(taps->h, H, (f8 ? 1 : 2) * Tk * h), "tap h");
     if (f8) HIPCHECK(ctx, cp(taps->h_scales, Hs, Tk * h / 32), "tap h scales");
-    if (!o_bf16) HIPCHECK(ctx, cp(taps->expert_out, O, 4 * Tk * le), "tap expert_out");
+    HIPCHECK(ctx, cp(taps->expert_out, O, 4 * Tk * le), "tap expert_out");
     if (!c.latent_moe) HIPCHECK(ctx, cp(taps->u, u, 4 * (size_t)T * le), "tap u");
     if (c.latent_moe && taps->n)
       HIPCHECK(ctx,

@@ -130,9 +130,8 @@ hipError_t launch_topk(const float* scores, const float* bias, int T, int E, int
 hipError_t launch_route(const int32_t* idx, int T, int E, int k, int32_t* counts, int32_t* offsets, int32_t* perm,
                         int32_t* inv, int32_t* scratch, hipStream_t s);
 int64_t route_scratch_bytes(int max_tokens, int E);
-// O: fp32, or bf16 when o_bf16. mode 0: n = bf16(gamma * u / sqrt(mean(u^2) + eps)) into n_out (ld ldn);
-// mode 1: u only
-hipError_t launch_combine(const void* O, bool o_bf16, const int32_t* inv, const float* p, int T, int k, int width,
+// mode 0: n = bf16(gamma * u / sqrt(mean(u^2) + eps)) into n_out (ld ldn); mode 1: u only
+hipError_t launch_combine(const float* O, const int32_t* inv, const float* p, int T, int k, int width,
                           const float* gamma, float eps, int mode, uint16_t* n_out, int64_t ldn, float* u_out,
                           hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);

@@ -1456,21 +1456,17 @@ hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) 
     case GEMM_DOWN: {
       const bool gu = stage == GEMM_GATEUP;
       const bool bf = a.a_fmt == A_BF16;
-      const int mode = gu ? (bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_MXFP8) : a.seg[0].mode;
+      const int mode = gu ? (bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_MXFP8) : EPI_F32;
       GemmArgs pa = a;  // the panel kernel's share
       if (tiled_grouped_ok(a, mode)) {
         if (gu && bf)
           launch_bf16_grouped<2, GEMM_GATEUP>(a, s);
         else if (gu)
           launch_f8<1, GEMM_GATEUP>(a, s);
-        else if (bf && mode == EPI_F32)
-          launch_bf16_grouped<0, GEMM_DOWN>(a, s);  // fp32 expert outputs: direct stores
         else if (bf)
-          launch_bf16_grouped<2, GEMM_DOWN>(a, s);  // other modes: the segment epilogue
-        else if (mode == EPI_F32)
-          launch_f8<0, GEMM_DOWN>(a, s);
+          launch_bf16_grouped<0, GEMM_DOWN>(a, s);
         else
-          launch_f8<2, GEMM_DOWN>(a, s);
+          launch_f8<0, GEMM_DOWN>(a, s);
         if (a.row_split == 1) break;  // no group left for the panel kernel
       } else {
         pa.row_split = 0;
@@ -1778,19 +1774,10 @@ constexpr int kCombineThreads = 256;
 constexpr int kMaxWidth = 8192;
 constexpr int kCombineChunks = kMaxWidth / (4 * kCombineThreads);  // float4 columns per thread, at most
 
-// Four consecutive expert outputs as fp32: fp32 as they are, bf16 (8 bytes) widened exactly.
-__device__ __forceinline__ float4 load4(const float* p) { return *(const float4*)p; }
-__device__ __forceinline__ float4 load4(const u16* p) {
-  const uint2 v = *(const uint2*)p;
-  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u), __uint_as_float(v.y << 16),
-                     __uint_as_float(v.y & 0xFFFF0000u));
-}
-
 // One block of 256 threads per token; thread tid holds columns 4 tid + 1024 i (i < 8) of u_t in
-// registers; the expert outputs O are fp32 or bf16 (OT). KC > 0: k fixed at compile time, so all of a
-// chunk's row loads are in flight at once.
-template <int KC, typename OT>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const OT* __restrict__ O,
+// registers. KC > 0: k fixed at compile time, so all of a chunk's row loads are in flight at once.
+template <int KC>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ O,
                                                                   const int32_t* __restrict__ inv,
                                                                   const float* __restrict__ p, int k, int width,
                                                                   const float* __restrict__ gamma, float eps, int mode,
@@ -1816,7 +1803,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const OT* __re
       if constexpr (KC > 0) {
         float4 o[KC];
 #pragma unroll
-        for (int jj = 0; jj < KC; ++jj) o[jj] = load4(O + (int64_t)rows[jj] * width + c);
+        for (int jj = 0; jj < KC; ++jj) o[jj] = *(const float4*)(O + (int64_t)rows[jj] * width + c);
 #pragma unroll
         for (int jj = 0; jj < KC; ++jj) {  // selection order, as the runtime-k loop
           const float w = pp[jj];
@@ -1827,7 +1814,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const OT* __re
         }
       } else {
         for (int jj = 0; jj < k; ++jj) {
-          const float4 o = load4(O + (int64_t)rows[jj] * width + c);
+          const float4 o = *(const float4*)(O + (int64_t)rows[jj] * width + c);
           const float w = pp[jj];
           a.x += w * o.x;
           a.y += w * o.y;
@@ -1861,29 +1848,19 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const OT* __re
   }
 }
 
-template <typename OT>
-static void launch_combine_t(const OT* O, const int32_t* inv, const float* p, int T, int k, int width,
-                             const float* gamma, float eps, int mode, uint16_t* n_out, int64_t ldn, float* u_out,
-                             hipStream_t s) {
-  if (k == 16)
-    hipLaunchKernelGGL((combine_kernel<16, OT>), dim3(T), dim3(kCombineThreads), 0, s, O, inv, p, k, width, gamma, eps,
-                       mode, n_out, ldn, u_out);
-  else if (k == 8)
-    hipLaunchKernelGGL((combine_kernel<8, OT>), dim3(T), dim3(kCombineThreads), 0, s, O, inv, p, k, width, gamma, eps,
-                       mode, n_out, ldn, u_out);
-  else
-    hipLaunchKernelGGL((combine_kernel<0, OT>), dim3(T), dim3(kCombineThreads), 0, s, O, inv, p, k, width, gamma, eps,
-                       mode, n_out, ldn, u_out);
-}
-
-hipError_t launch_combine(const void* O, bool o_bf16, const int32_t* inv, const float* p, int T, int k, int width,
+hipError_t launch_combine(const float* O, const int32_t* inv, const float* p, int T, int k, int width,
                           const float* gamma, float eps, int mode, uint16_t* n_out, int64_t ldn, float* u_out,
                           hipStream_t s) {
   if (width > kMaxWidth || k > 64 || width % 4 || (mode == 0 && ldn % 4)) return hipErrorInvalidValue;
-  if (o_bf16)
-    launch_combine_t((const u16*)O, inv, p, T, k, width, gamma, eps, mode, n_out, ldn, u_out, s);
+  if (k == 16)
+    hipLaunchKernelGGL(combine_kernel<16>, dim3(T), dim3(kCombineThreads), 0, s, O, inv, p, k, width, gamma, eps, mode,
+                       n_out, ldn, u_out);
+  else if (k == 8)
+    hipLaunchKernelGGL(combine_kernel<8>, dim3(T), dim3(kCombineThreads), 0, s, O, inv, p, k, width, gamma, eps, mode,
+                       n_out, ldn, u_out);
   else
-    launch_combine_t((const float*)O, inv, p, T, k, width, gamma, eps, mode, n_out, ldn, u_out, s);
+    hipLaunchKernelGGL(combine_kernel<0>, dim3(T), dim3(kCombineThreads), 0, s, O, inv, p, k, width, gamma, eps, mode,
+                       n_out, ldn, u_out);
   return hipGetLastError();
 }
 
