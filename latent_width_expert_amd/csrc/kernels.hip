@@ -1774,6 +1774,12 @@ constexpr int kCombineThreads = 256;
 constexpr int kMaxWidth = 8192;
 constexpr int kCombineChunks = kMaxWidth / (4 * kCombineThreads);  // float4 columns per thread, at most
 
+// Four consecutive expert outputs, loaded non-temporal: each is read once (-11% at 8192 tokens).
+__device__ __forceinline__ float4 load4_nt(const float* p) {
+  return make_float4(__builtin_nontemporal_load(p), __builtin_nontemporal_load(p + 1), __builtin_nontemporal_load(p + 2),
+                     __builtin_nontemporal_load(p + 3));
+}
+
 // One block of 256 threads per token; thread tid holds columns 4 tid + 1024 i (i < 8) of u_t in
 // registers. KC > 0: k fixed at compile time, so all of a chunk's row loads are in flight at once.
 template <int KC>
@@ -1803,7 +1809,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
       if constexpr (KC > 0) {
         float4 o[KC];
 #pragma unroll
-        for (int jj = 0; jj < KC; ++jj) o[jj] = *(const float4*)(O + (int64_t)rows[jj] * width + c);
+        for (int jj = 0; jj < KC; ++jj) o[jj] = load4_nt(O + (int64_t)rows[jj] * width + c);
 #pragma unroll
         for (int jj = 0; jj < KC; ++jj) {  // selection order, as the runtime-k loop
           const float w = pp[jj];
@@ -1814,7 +1820,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
         }
       } else {
         for (int jj = 0; jj < k; ++jj) {
-          const float4 o = *(const float4*)(O + (int64_t)rows[jj] * width + c);
+          const float4 o = load4_nt(O + (int64_t)rows[jj] * width + c);
           const float w = pp[jj];
           a.x += w * o.x;
           a.y += w * o.y;
