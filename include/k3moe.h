@@ -187,6 +187,19 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
                      void* stream, const k3moe_taps* taps);
 
 /*
+ * Quantile Balancing: the router bias b of eq. 13 from per-expert router-score quantiles ("Serving
+ * K3, 01 architecture", hot-expert paragraph; "Kimi K3: architectural innovations", "A router
+ * decision is also a scheduling decision": allocation thresholds follow the observed score
+ * distribution). The pages give no formula; reading taken: over a calibration batch of T tokens,
+ * b_e = -(the m-th largest of expert e's scores), m = round(T k / E) (halves up, within [1, T]),
+ * so that s + b >= 0 for exactly m tokens per expert (ties aside).
+ * scores_dev: fp32 [T, E] row-major (e.g. the `scores` tap of a forward over the batch);
+ * bias_dev: fp32 [E] out, on the stream. 1 <= T <= 16384 (else K3MOE_ETOOBIG); null pointers give
+ * K3MOE_EINVAL. The result can be packed as the router bias (k3moe_weights.router_bias).
+ */
+int k3moe_quantile_bias(k3moe_ctx* ctx, const float* scores_dev, int32_t T, float* bias_dev, void* stream);
+
+/*
  * Per-stage timing. k3moe_profile_begin makes the next forward calls (at most max_calls) record
  * a HIP event before and after each stage on their stream. k3moe_profile_end waits for those
  * events, writes the summed milliseconds of each stage to ms[0 .. n_stages-1] (n_stages =

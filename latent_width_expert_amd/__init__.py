@@ -83,6 +83,8 @@ def lib():
         L.k3moe_forward_ex.restype = ctypes.c_int
         L.k3moe_profile_begin.argtypes = [_vp, _i32]
         L.k3moe_profile_begin.restype = ctypes.c_int
+        L.k3moe_quantile_bias.argtypes = [_vp, _vp, _i32, _vp, _vp]
+        L.k3moe_quantile_bias.restype = ctypes.c_int
         L.k3moe_profile_end.argtypes = [_vp, ctypes.POINTER(ctypes.c_float), _i32, ctypes.POINTER(_i32)]
         L.k3moe_profile_end.restype = ctypes.c_int
         L.k3moe_stage_count.argtypes = []
@@ -223,6 +225,14 @@ class K3MoE:
 
     def last_error(self) -> str:
         return self._L.k3moe_last_error(self._h).decode()
+
+    def quantile_bias(self, scores, stream=None):
+        """Router bias b [E] (fp32, device) from router scores [T, E] (fp32, device) of a calibration
+        batch: k3moe_quantile_bias."""
+        assert scores.is_cuda and scores.dtype == torch.float32 and scores.dim() == 2 and scores.is_contiguous()
+        bias = torch.empty(scores.shape[1], dtype=torch.float32, device=scores.device)
+        self._check(self._L.k3moe_quantile_bias(self._h, _ptr(scores), scores.shape[0], _ptr(bias), _stream(stream)))
+        return bias
 
     def profile_begin(self, max_calls: int):
         self._check(self._L.k3moe_profile_begin(self._h, max_calls))

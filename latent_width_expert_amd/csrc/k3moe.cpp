@@ -328,6 +328,16 @@ int k3moe_pack_weights(k3moe_ctx* ctx, const k3moe_weights* wts, void* packed_de
   return K3MOE_OK;
 }
 
+int k3moe_quantile_bias(k3moe_ctx* ctx, const float* scores_dev, int32_t T, float* bias_dev, void* stream) {
+  if (!ctx) return K3MOE_EINVAL;
+  if (!scores_dev || !bias_dev) return fail(ctx, K3MOE_EINVAL, "scores and bias must be non-null");
+  if (T < 1 || T > 16384) return fail(ctx, K3MOE_ETOOBIG, "calibration batch T = %d outside [1, 16384]", T);
+  const int64_t E = ctx->cfg.n_experts, k = ctx->cfg.top_k;
+  const int m = (int)std::min<int64_t>(T, std::max<int64_t>(1, (2 * (int64_t)T * k + E) / (2 * E)));
+  HIPCHECK(ctx, launch_quantile_bias(scores_dev, T, (int)E, m, bias_dev, (hipStream_t)stream), "quantile bias launch");
+  return K3MOE_OK;
+}
+
 int k3moe_profile_begin(k3moe_ctx* ctx, int32_t max_calls) {
   if (!ctx) return K3MOE_EINVAL;
   if (max_calls < 1 || max_calls > 100000) return fail(ctx, K3MOE_EINVAL, "max_calls must be in [1, 100000]");

@@ -135,5 +135,7 @@ hipError_t launch_combine(const float* O, const int32_t* inv, const float* p, in
                           const float* gamma, float eps, int mode, uint16_t* n_out, int64_t ldn, float* u_out,
                           hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
+// b_e = -(m-th largest of scores[:, e]) for T <= 16384 calibration tokens ([T, E] fp32 scores)
+hipError_t launch_quantile_bias(const float* scores, int T, int E, int m, float* bias, hipStream_t s);
 
 }  // namespace k3

@@ -1870,6 +1870,55 @@ hipError_t launch_combine(const float* O, const int32_t* inv, const float* p, in
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------------
+// Quantile Balancing ("Serving K3, 01 architecture", hot-expert paragraph; "Kimi K3: architectural
+// innovations", "A router decision is also a scheduling decision"): expert allocation from
+// router-score quantiles, read as b_e = -(the m-th largest score of expert e over a calibration
+// batch), m = round(T k / E). One block per expert: the expert's T scores as order-preserving
+// 32-bit keys in LDS, a bitonic sort into descending order (padding keys 0 sort last), then the
+// key at rank m. The result is one of the scores, exactly.
+// ---------------------------------------------------------------------------------------------
+constexpr int kBalanceMaxTokens = 16384;
+
+__device__ __forceinline__ u32 order_key(float f) {  // monotone in f (finite values)
+  const u32 u = __float_as_uint(f);
+  return u ^ ((u >> 31) ? 0xFFFFFFFFu : 0x80000000u);
+}
+__device__ __forceinline__ float from_order_key(u32 k) {
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+__global__ __launch_bounds__(1024) void quantile_bias_kernel(const float* __restrict__ scores, int T, int E, int m,
+                                                             float* __restrict__ bias) {
+  __shared__ u32 keys[kBalanceMaxTokens];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  int n = 1;
+  while (n < T) n <<= 1;  // uniform; n <= kBalanceMaxTokens (host check)
+  for (int i = tid; i < n; i += 1024) keys[i] = i < T ? order_key(scores[(int64_t)i * E + e]) : 0u;
+  __syncthreads();
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < n / 2; i += 1024) {
+        const int lo = 2 * stride * (i / stride) + i % stride, hi = lo + stride;
+        const bool desc = (lo & size) == 0;  // the merge directions that leave the whole array descending
+        const u32 a = keys[lo], b = keys[hi];
+        if ((a < b) == desc) {
+          keys[lo] = b;
+          keys[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (tid == 0) bias[e] = -from_order_key(keys[m - 1]);
+}
+
+hipError_t launch_quantile_bias(const float* scores, int T, int E, int m, float* bias, hipStream_t s) {
+  if (T < 1 || T > kBalanceMaxTokens || E < 1 || m < 1 || m > T) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quantile_bias_kernel, dim3((unsigned)E), dim3(1024), 0, s, scores, T, E, m, bias);
+  return hipGetLastError();
+}
+
 __global__ void f32_to_bf16_kernel(const float* __restrict__ in, u16* __restrict__ out, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) out[i] = (u16)bf16_rne(in[i]);
