@@ -72,6 +72,8 @@ typedef struct {
   int32_t act;            /* K3MOE_ACT_BF16 or K3MOE_ACT_MXFP8 for the routed GEMM inputs z, h */
   int32_t max_tokens;     /* largest T a forward call may pass (sizes the workspace) */
   float rms_eps;          /* epsilon inside the RMSNorm square root */
+  int32_t lora_rank;      /* r of the BF16 LoRA deltas on every routed expert matrix: 0 (none) or a
+                             multiple of 8 up to 32 */
 } k3moe_config;
 
 /* One canonical MXFP4 matrix on the device (layout in the header comment). */
@@ -79,6 +81,22 @@ typedef struct {
   const void* codes;
   const void* scales;
 } k3moe_mx;
+
+/*
+ * BF16 LoRA deltas of one routed expert ("Serving K3, 01 architecture": fine-tuning ships BF16 LoRA
+ * deltas over the MXFP4 base weights). Each expert matrix W [N, K] becomes W + B A with A [r, K] and
+ * B [N, r], both bf16 row-major device arrays (r = lora_rank; any scaling folded into B):
+ *   a_gate, a_up [r, le]; b_gate, b_up [hidden, r]; a_down [r, hidden]; b_down [le, r].
+ * The product is applied as B (A v) in fp32 on the activation v the base matrix sees.
+ */
+typedef struct {
+  const void* a_gate;
+  const void* b_gate;
+  const void* a_up;
+  const void* b_up;
+  const void* a_down;
+  const void* b_down;
+} k3moe_lora;
 
 /*
  * Weights handed to k3moe_pack_weights. A call packs the dense part when include_dense != 0 and
@@ -105,6 +123,7 @@ typedef struct {
   const k3moe_mx* gate;     /* host arrays of routed_count entries */
   const k3moe_mx* up;
   const k3moe_mx* down;
+  const k3moe_lora* lora;   /* host array of routed_count entries; required when lora_rank > 0 */
 } k3moe_weights;
 
 /*
@@ -185,6 +204,46 @@ int k3moe_forward(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, voi
 /* k3moe_forward plus copies of the intermediates requested in `taps` (may be NULL). */
 int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, void* workspace_dev,
                      void* stream, const k3moe_taps* taps);
+
+/*
+ * Expert-parallel split of a forward ("Serving K3, 01 architecture": expert parallelism is mandatory
+ * at scale and its all-to-all has data-dependent sizes; "Kimi K3: architectural innovations",
+ * "Compress the expert interface": the latent z is what crosses the interconnect). With the experts in
+ * n_ranks contiguous ranges of E / n_ranks, forward = head, then on each rank the experts of its range
+ * on the rows it receives, then tail at the tokens' origin. On one GPU the three calls reproduce
+ * k3moe_forward (the same kernels run on the same rows).
+ *
+ * k3moe_forward_head: router, top-k, dispatch tables, W_down and the shared hiddens for T tokens, then
+ *   the send side: send_rows_dev [T k, le] the routed input of every (token, slot) in dispatched order
+ *   (expert ascending, token ascending; bf16, or E4M3 codes with send_scales_dev [T k, le / 32] E8M0
+ *   for MXFP8 activations, else send_scales_dev may be NULL), send_counts_dev int32 [n_ranks] the rows
+ *   for each rank (rank i holds experts [i E / n_ranks, (i + 1) E / n_ranks); its rows are
+ *   send_rows[sum of earlier counts ..]) and expert_counts_dev int32 [E] rows per expert (may be NULL).
+ *   n_ranks divides E. The workspace keeps the routing state the tail needs: pass the same one to
+ *   k3moe_forward_tail and do not use it for another call in between.
+ * k3moe_experts_forward: on a context holding one rank's experts (n_experts = E / n_ranks, routed
+ *   experts packed; the dense part is not needed), the routed experts on R received rows: rows_dev
+ *   [R, le] expert-contiguous (expert_counts_dev int32 [n_experts] rows each, in expert order), with
+ *   row_scales_dev [R, le / 32] for MXFP8; out_dev fp32 [R, le] the expert outputs in the same order.
+ *   0 <= R <= max_tokens * top_k; workspace_dev of k3moe_workspace_bytes.
+ * k3moe_forward_tail: combine (eq. 11) of the expert outputs expert_out_dev fp32 [T k, le] (in the
+ *   order of the head's send rows), RMSNorm, W_up and the shared experts' down projections -> y_dev.
+ */
+int k3moe_forward_head(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* workspace_dev, void* stream,
+                       int32_t n_ranks, void* send_rows_dev, uint8_t* send_scales_dev, int32_t* send_counts_dev,
+                       int32_t* expert_counts_dev);
+int k3moe_experts_forward(k3moe_ctx* ctx, const void* rows_dev, const uint8_t* row_scales_dev, int32_t R,
+                          const int32_t* expert_counts_dev, float* out_dev, void* workspace_dev, void* stream);
+int k3moe_forward_tail(k3moe_ctx* ctx, const float* expert_out_dev, int32_t T, void* y_dev, void* workspace_dev,
+                       void* stream);
+
+/*
+ * Measurement aid, not part of the layer: reads `bytes` (a multiple of 16) of device memory once with
+ * non-temporal 16-byte loads and xors a checksum of every word into *out_dev (uint32, device). Timing
+ * it gives the HBM read rate a plain streaming kernel reaches, the practical ceiling the layer's
+ * weight streams are compared with.
+ */
+int k3moe_stream_read(const void* buf_dev, size_t bytes, uint32_t* out_dev, void* stream);
 
 /*
  * Quantile Balancing: the router bias b of eq. 13 from per-expert router-score quantiles ("Serving

@@ -107,6 +107,16 @@ struct GemmArgs {
   EpiSeg seg[kMaxSeg];
   float* partial;          // dense launches of few rows: split-K partial sums (workspace), may be null
   int64_t partial_bytes;   // at least gemm_partial_bytes() to be used
+  // BF16 LoRA delta of a grouped stage (lora_t null: none). Output column n of group g in row `row`
+  // gains sum_{q < lora_rank} lora_t[row * lora_ldt + q0 + q] * B[n * lora_ldb + q0 + q], with
+  // B = lora_b + g * lora_b_stride (bf16) and q0 = lora_rank for the up units of GLU panels, else 0.
+  const float* lora_t;
+  int32_t lora_ldt;
+  int32_t lora_rank;       // a multiple of 8
+  const uint16_t* lora_b;
+  int64_t lora_b_stride;   // elements between groups
+  int32_t lora_ldb;        // elements per row of B
+  int32_t pad2_;
 };
 
 enum GemmStage : int { GEMM_X = 0, GEMM_GATEUP = 1, GEMM_DOWN = 2, GEMM_Y = 3 };
@@ -135,6 +145,42 @@ hipError_t launch_combine(const float* O, const int32_t* inv, const float* p, in
                           const float* gamma, float eps, int mode, uint16_t* n_out, int64_t ldn, float* u_out,
                           hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
+
+// LoRA first factor of a grouped stage: t[row, n] = sum_k act[row, k] La_g[n, k] over the rows of each
+// group g (La bf16 [N, K] per group, la_stride elements apart, N <= 64 and a multiple of 8); the
+// activation rows are bf16 or MXFP8 (codes + E8M0 scales), addressed through the optional row map.
+struct LoraAArgs {
+  const void* A;
+  int64_t lda;
+  int64_t a_bytes;
+  const uint8_t* A_scales;
+  int64_t ldas;
+  int64_t as_bytes;
+  int32_t a_fmt;
+  int32_t n_groups;
+  const int32_t* rowmap;
+  const int32_t* offsets;
+  const uint16_t* La;
+  int64_t la_stride;
+  int32_t N, K;
+  float* t;
+  int64_t ldt;
+};
+hipError_t launch_lora_a(const LoraAArgs& a, hipStream_t s);
+
+// Expert-parallel send side: rows[r] = src[perm[r]] for r < n_rows (row_bytes each, a multiple of 16),
+// and the MXFP8 scale rows likewise (scale_bytes each, may be 0); send_counts[i] = offsets[(i + 1) per]
+// - offsets[i per] for i < n_ranks.
+hipError_t launch_gather_rows(const uint8_t* src, int64_t row_bytes, const uint8_t* src_scales, int64_t scale_bytes,
+                              const int32_t* perm, int64_t n_rows, uint8_t* rows, uint8_t* scales, hipStream_t s);
+hipError_t launch_send_counts(const int32_t* offsets, int n_ranks, int per, int32_t* send_counts, hipStream_t s);
+// offsets[0..E] = exclusive prefix sum of max(counts[e], 0), each clamped to `limit` (one block)
+hipError_t launch_offsets(const int32_t* counts, int E, int64_t limit, int32_t* offsets, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t s);
+
+// Streaming read of `bytes` (a multiple of 16) with non-temporal 16-byte loads; the xor of every word
+// read is xor-ed into *out (a measurement of the plain HBM read rate).
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s);
 // b_e = -(m-th largest of scores[:, e]) for T <= 16384 calibration tokens ([T, E] fp32 scores)
 hipError_t launch_quantile_bias(const float* scores, int T, int E, int m, float* bias, hipStream_t s);
 

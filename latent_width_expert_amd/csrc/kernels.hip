@@ -277,9 +277,39 @@ __device__ __forceinline__ void mxfp8_block(float v0, float v1, u32& c0, u32& c1
   c1 = (pk >> 8) & 0xFFu;
 }
 
-// Epilogue of one 16-row tile (rows mb .. mb + 15, valid below r1) of one panel.
-__device__ __forceinline__ void epilogue(const GemmArgs& args, const f32x4 (&acc)[4], int panel, int mb, int r1,
-                                         int lane) {
+// sum_{q < rank} t[q] b[q] in fp32, q ascending (rank a multiple of 8; t 32-byte and b 16-byte aligned):
+// one output column's BF16 LoRA delta, t the row's first-factor values, b the column's row of B.
+__device__ __forceinline__ float lora_dot(const float* t, const uint16_t* b, int rank) {
+  float s = 0.0f;
+  for (int q = 0; q < rank; q += 8) {
+    const float4 t0 = *(const float4*)(t + q), t1 = *(const float4*)(t + q + 4);
+    const u32x4 bb = *(const u32x4*)(b + q);
+    s = fmaf(t0.x, __uint_as_float(bb[0] << 16), s);
+    s = fmaf(t0.y, __uint_as_float(bb[0] & 0xFFFF0000u), s);
+    s = fmaf(t0.z, __uint_as_float(bb[1] << 16), s);
+    s = fmaf(t0.w, __uint_as_float(bb[1] & 0xFFFF0000u), s);
+    s = fmaf(t1.x, __uint_as_float(bb[2] << 16), s);
+    s = fmaf(t1.y, __uint_as_float(bb[2] & 0xFFFF0000u), s);
+    s = fmaf(t1.z, __uint_as_float(bb[3] << 16), s);
+    s = fmaf(t1.w, __uint_as_float(bb[3] & 0xFFFF0000u), s);
+  }
+  return s;
+}
+
+// LoRA deltas of one 16 x 16 output block held as acc[r] (lane rows row0 + r, r < 4, valid while below
+// r1; column col of the group's B, q0 its first rank index). Uniform branch on args.lora_t outside.
+__device__ __forceinline__ void lora_add(const GemmArgs& args, f32x4& acc, int grp, int row0, int r1, int col, int q0) {
+  const uint16_t* b = args.lora_b + (int64_t)grp * args.lora_b_stride + (int64_t)col * args.lora_ldb + q0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = row0 + r;
+    if (row < r1) acc[r] += lora_dot(args.lora_t + (int64_t)row * args.lora_ldt + q0, b, args.lora_rank);
+  }
+}
+
+// Epilogue of one 16-row tile (rows mb .. mb + 15, valid below r1) of one panel of group grp.
+__device__ __forceinline__ void epilogue(const GemmArgs& args, const f32x4 (&acc_in)[4], int panel, int mb, int r1,
+                                         int lane, int grp) {
   int si = 0;
   for (int s = 0; s < args.nseg; ++s)
     if (panel >= args.seg[s].p0 && panel < args.seg[s].p1) si = s;
@@ -287,6 +317,23 @@ __device__ __forceinline__ void epilogue(const GemmArgs& args, const f32x4 (&acc
   const int j = lane & 15, gq = lane >> 4;
   const int pl = panel - sg.p0;
   const int mode = sg.mode;
+  f32x4 acc[4] = {acc_in[0], acc_in[1], acc_in[2], acc_in[3]};
+  if (args.lora_t) {
+    if (mode == EPI_SWIGLU_BF16 || mode == EPI_SWIGLU_MXFP8) {
+      // row-tiles: gate and up of units 32 pl + j, then of units 32 pl + 16 + j
+      const int R = args.lora_rank;
+      lora_add(args, acc[0], grp, mb + 4 * gq, r1, 32 * pl + j, 0);
+      lora_add(args, acc[1], grp, mb + 4 * gq, r1, 32 * pl + j, R);
+      lora_add(args, acc[2], grp, mb + 4 * gq, r1, 32 * pl + 16 + j, 0);
+      lora_add(args, acc[3], grp, mb + 4 * gq, r1, 32 * pl + 16 + j, R);
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int col = 64 * pl + 16 * rt + j;
+        if (col < sg.ncols) lora_add(args, acc[rt], grp, mb + 4 * gq, r1, col, 0);
+      }
+    }
+  }
   if (mode == EPI_SWIGLU_BF16 || mode == EPI_SWIGLU_MXFP8 || mode == EPI_MXFP8) {
     const bool glu = mode != EPI_MXFP8;
     const int nblk = glu ? 1 : 2;  // 32-wide blocks per panel: GLU 32 units, plain 64 columns
@@ -492,7 +539,7 @@ __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_ker
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) tile[rt] = acc[m2][rt];
           }
-        epilogue(args, tile, panel, mb + 16 * mt, r1, lane);
+        epilogue(args, tile, panel, mb + 16 * mt, r1, lane, grp);
       }
     }
   }
@@ -790,7 +837,8 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
   };
   f32x4 acc[MTW][PPW][4];
   // the epilogue of a unit (its rows, group end and panels given; the accumulators as they stand)
-  auto finish = [&](const int mb, const int r1, const int panel0, const int npan) __attribute__((always_inline)) {
+  auto finish = [&](const int mb, const int r1, const int panel0, const int npan, const int grp)
+                    __attribute__((always_inline)) {
       // epilogue; lane indices re-derived (opaque to the compiler) so that no address arithmetic is
       // hoisted out of the chunk loop
       int ln = lane;
@@ -798,6 +846,28 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
       const int eg = ln >> 4, ej = ln & 15;
       const EpiSeg& sg = args.seg[0];
       const int nrow = min(ROWS, r1 - mb);
+      // BF16 LoRA deltas (grouped stages), added to the accumulators before the epilogue proper; the
+      // segment epilogue (EPI 2) adds them itself
+      if constexpr (EPI != 2 && !DENSE) {
+        if (args.lora_t) {
+          #pragma unroll
+          for (int j = 0; j < MTW; ++j)
+            #pragma unroll
+            for (int pp = 0; pp < PPW; ++pp) {
+              const int pl = PPW * pg + pp;
+              const int row0 = mb + 16 * (h + NPH * j) + 4 * eg;
+              if (pl < npan && row0 < r1) {
+                #pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                  // EPI 1 (GLU panels): row-tiles gate / up of units 32 p + ej, then of 32 p + 16 + ej
+                  const int col = EPI == 1 ? 32 * (panel0 + pl) + 16 * (ct >> 1) + ej : 64 * (panel0 + pl) + 16 * ct + ej;
+                  const int q0 = EPI == 1 && (ct & 1) ? args.lora_rank : 0;
+                  if (EPI == 1 || col < sg.ncols) lora_add(args, acc[j][pp][ct], grp, row0, r1, col, q0);
+                }
+              }
+            }
+        }
+      }
       if constexpr (EPI == 1) {
         // codes staged as [ROWS][128 bytes] (32 units per panel), scales as [ROWS][4]
         uint8_t* stg = &lds_a[NA - 1][0];  // A stage NA - 1: no prologue DMA writes it
@@ -854,7 +924,7 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
           ([&] {
             constexpr int j = JP / PPW, pp = JP % PPW;
             if (PPW * pg + pp < npan && 16 * (h + NPH * j) < nrow)
-              epilogue(args, acc[j][pp], panel0 + PPW * pg + pp, mb + 16 * (h + NPH * j), r1, ln);
+              epilogue(args, acc[j][pp], panel0 + PPW * pg + pp, mb + 16 * (h + NPH * j), r1, ln, grp);
           }(), ...);
         }(std::make_integer_sequence<int, MTW * PPW>{});
       } else {
@@ -1001,10 +1071,10 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
       // The next unit's prologue DMAs go out before this unit's epilogue (into A stages 0 .. DA - 1 and
       // the B stages; the epilogue stages in A stage NA - 1), so the memory path keeps working while
       // the epilogue computes; the full drain below holds whatever order loads and stores finish in.
-      const int e_mb = mb, e_r1 = r1, e_panel0 = panel0, e_npan = npan;
+      const int e_mb = mb, e_r1 = r1, e_panel0 = panel0, e_npan = npan, e_grp = grp;
       have = next_unit();
       if (have) prologue();
-      finish(e_mb, e_r1, e_panel0, e_npan);
+      finish(e_mb, e_r1, e_panel0, e_npan, e_grp);
       wait_vmcnt<0>();
       __syncthreads();  // staging and rings are reused by the next unit
   }
@@ -1265,7 +1335,7 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs args, int G
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) acc[ct] += v[c][ct];
   }
-  epilogue(args, acc, panel, 16 * t, min(args.M, kSkinnyRows), lane);
+  epilogue(args, acc, panel, 16 * t, min(args.M, kSkinnyRows), lane, 0);
 }
 
 template <int KSPLIT, int AFMT, int NBUF, int MT, bool AHEAD, int TAG>
@@ -1927,6 +1997,245 @@ __global__ void f32_to_bf16_kernel(const float* __restrict__ in, u16* __restrict
 hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, in, out, n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// BF16 LoRA deltas over the MXFP4 experts ("Serving K3, 01 architecture": fine-tuning ships bf16 LoRA
+// deltas over the 4-bit base). The first factor t = act La^T of a grouped stage (rank columns per
+// matrix); the second factor is added in the grouped GEMMs' epilogues (lora_add).
+// One block of 4 waves per group: the group's rows in chunks of 64 (4 row tiles of 16); wave w takes
+// K windows w, w + 4, ... of 128; per window, lane (i, g) holds K [128 w + 32 g, +32) of row / column i
+// and four bf16 MFMA 16x16x32 steps cover it. The four waves' sums are added in wave order through
+// LDS (deterministic).
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ void lora_act_load(const LoraAArgs& a, rsrc_t ar, rsrc_t asr, int arow, bool ok, int kb,
+                                              bf16x8 (&v)[4]) {
+  const bool in = ok && kb * 32 < a.K;
+  if (a.a_fmt == A_BF16) {
+    const int off = in ? (arow * (int)a.lda + kb * 32) * 2 : kOOB;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) v[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ar, off + 16 * st, 0, 0));
+  } else {
+    const int off = in ? arow * (int)a.lda + kb * 32 : kOOB;
+    const u32x4 c0 = __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0);
+    const u32x4 c1 = __builtin_amdgcn_raw_buffer_load_b128(ar, off + 16, 0, 0);
+    const float sc = e8m0_f32(__builtin_amdgcn_raw_buffer_load_b8(asr, in ? arow * (int)a.ldas + kb : kOOB, 0, 0));
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const u32 d0 = st < 2 ? c0[2 * st] : c1[2 * st - 4];
+      const u32 d1 = st < 2 ? c0[2 * st + 1] : c1[2 * st - 3];
+      u32x4 r;
+      r[0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, false));
+      r[1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, true));
+      r[2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, sc, false));
+      r[3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, sc, true));
+      v[st] = __builtin_bit_cast(bf16x8, r);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void lora_a_kernel(LoraAArgs a) {
+  __shared__ f32x4 red[3][4][4][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = blockIdx.x;
+  const int r0 = a.offsets[grp], r1 = a.offsets[grp + 1];
+  if (r0 >= r1) return;  // uniform
+  const int i16 = lane & 15, g = lane >> 4;
+  const int nwin = (a.K + kWinK - 1) / kWinK;
+  const int nct = (a.N + 15) / 16;
+  const rsrc_t ar = make_rsrc(a.A, a.a_bytes);
+  const rsrc_t asr = make_rsrc(a.A_scales, a.A_scales ? a.as_bytes : 0);
+  const rsrc_t lr = make_rsrc(a.La + (int64_t)grp * a.la_stride, (int64_t)a.N * a.K * 2);
+  for (int mb = r0; mb < r1; mb += 64) {
+    const int nrt = min(4, (r1 - mb + 15) / 16);
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int arow[4];
+    bool aok[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int row = mb + 16 * rt + i16;
+      aok[rt] = rt < nrt && row < r1;
+      arow[rt] = aok[rt] ? (a.rowmap ? a.rowmap[row] : row) : 0;
+    }
+    for (int w = wv; w < nwin; w += 4) {
+      const int kb = 4 * w + g;
+      bf16x8 bv[4][4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int n = 16 * ct + i16;
+        const int off = ct < nct && n < a.N && kb * 32 < a.K ? (n * a.K + kb * 32) * 2 : kOOB;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) bv[ct][st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(lr, off + 16 * st, 0, 0));
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        if (rt < nrt) {  // uniform
+          bf16x8 av[4];
+          lora_act_load(a, ar, asr, arow[rt], aok[rt], kb, av);
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+              if (ct < nct) acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[st], bv[ct][st], acc[rt][ct], 0, 0, 0);
+        }
+      }
+    }
+    if (wv > 0) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) red[wv - 1][rt][ct][lane] = acc[rt][ct];
+    }
+    __syncthreads();
+    if (wv == 0) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          f32x4 v = acc[rt][ct];
+#pragma unroll
+          for (int q = 0; q < 3; ++q) v += red[q][rt][ct][lane];
+          // D lane (j, g): column 16 ct + j, rows 16 rt + 4 g + r
+          const int n = 16 * ct + i16;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = mb + 16 * rt + 4 * g + r;
+            if (rt < nrt && row < r1 && n < a.N) a.t[(int64_t)row * a.ldt + n] = v[r];
+          }
+        }
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_lora_a(const LoraAArgs& a, hipStream_t s) {
+  if (a.n_groups <= 0) return hipSuccess;
+  if (a.N < 8 || a.N > 64 || a.N % 8 || a.K % 32 || a.K <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lora_a_kernel, dim3((unsigned)a.n_groups), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Expert-parallel send side ("Serving K3, 01 architecture": expert parallelism with an all-to-all of
+// data-dependent sizes; "Kimi K3: architectural innovations", "Compress the expert interface": the
+// dispatched payload is the latent). With the experts in contiguous ranges per rank, the dispatched
+// (expert-contiguous) rows are already grouped by destination: the send buffer is the routed input
+// gathered in that order, and rank i's share is the rows of its expert range.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ src, int64_t row_bytes,
+                                                          const uint8_t* __restrict__ src_scales, int64_t scale_bytes,
+                                                          const int32_t* __restrict__ perm, int64_t n_rows,
+                                                          uint8_t* __restrict__ rows, uint8_t* __restrict__ scales) {
+  for (int64_t r = blockIdx.x; r < n_rows; r += gridDim.x) {
+    const int64_t from = perm[r];
+    const u32x4* s4 = (const u32x4*)(src + from * row_bytes);
+    u32x4* d4 = (u32x4*)(rows + r * row_bytes);
+    for (int64_t c = threadIdx.x; c < row_bytes / 16; c += 256) d4[c] = s4[c];
+    for (int64_t c = threadIdx.x; c < scale_bytes; c += 256) scales[r * scale_bytes + c] = src_scales[from * scale_bytes + c];
+  }
+}
+
+hipError_t launch_gather_rows(const uint8_t* src, int64_t row_bytes, const uint8_t* src_scales, int64_t scale_bytes,
+                              const int32_t* perm, int64_t n_rows, uint8_t* rows, uint8_t* scales, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  if (row_bytes % 16 || (scale_bytes > 0 && (!src_scales || !scales))) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)std::min<int64_t>(n_rows, 8192);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(grid), dim3(256), 0, s, src, row_bytes, src_scales, scale_bytes, perm,
+                     n_rows, rows, scales);
+  return hipGetLastError();
+}
+
+__global__ void send_counts_kernel(const int32_t* __restrict__ offsets, int n_ranks, int per,
+                                   int32_t* __restrict__ send_counts) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n_ranks) send_counts[i] = offsets[(i + 1) * per] - offsets[i * per];
+}
+
+hipError_t launch_send_counts(const int32_t* offsets, int n_ranks, int per, int32_t* send_counts, hipStream_t s) {
+  if (n_ranks <= 0 || per <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(send_counts_kernel, dim3((unsigned)ceil_div(n_ranks, 64)), dim3(64), 0, s, offsets, n_ranks, per,
+                     send_counts);
+  return hipGetLastError();
+}
+
+// Expert row ranges from received counts: like route_offsets_kernel, with negative counts taken as zero
+// and every offset clamped to the rows actually received.
+__global__ __launch_bounds__(kRouteThreads) void offsets_clamped_kernel(int E, const int32_t* __restrict__ counts,
+                                                                        int64_t limit, int32_t* __restrict__ offsets) {
+  __shared__ int64_t part[kRouteThreads];
+  const int tid = threadIdx.x;
+  const int per = (E + kRouteThreads - 1) / kRouteThreads;
+  const int e0 = tid * per, e1 = min(E, e0 + per);
+  int64_t run = 0;
+  for (int e = e0; e < e1; ++e) run += max(counts[e], 0);
+  part[tid] = run;
+  __syncthreads();
+  for (int off = 1; off < kRouteThreads; off <<= 1) {
+    const int64_t v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int64_t acc = part[tid] - run;
+  for (int e = e0; e < e1; ++e) {
+    offsets[e] = (int32_t)min(acc, limit);
+    acc += max(counts[e], 0);
+  }
+  if (tid == kRouteThreads - 1) offsets[E] = (int32_t)min(part[kRouteThreads - 1], limit);
+}
+
+hipError_t launch_offsets(const int32_t* counts, int E, int64_t limit, int32_t* offsets, hipStream_t s) {
+  if (E < 1 || E > kMaxExperts || limit < 0 || limit > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(offsets_clamped_kernel, dim3(1), dim3(kRouteThreads), 0, s, E, counts, limit, offsets);
+  return hipGetLastError();
+}
+
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, p, n, value);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Plain streaming read (measurement of the HBM read rate a simple kernel reaches): every 16 bytes
+// read once with non-temporal loads, four loads in flight per thread, the xor of all words folded
+// into one word (so that no load is dead).
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void stream_read_kernel(const void* buf, int64_t n16, uint32_t* out) {
+  const u32x4* p = (const u32x4*)buf;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  u32 acc = 0;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(p + i), b = __builtin_nontemporal_load(p + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride), d = __builtin_nontemporal_load(p + i + 3 * stride);
+    const u32x4 x = a ^ b ^ c ^ d;
+    acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = __builtin_nontemporal_load(p + i);
+    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  }
+  for (int off = 32; off >= 1; off >>= 1) acc ^= (u32)__shfl_xor((int)acc, off);
+  if ((threadIdx.x & 63) == 0) atomicXor(out, acc);
+}
+
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s) {
+  if (bytes <= 0 || bytes % 16 || !buf || !out) return hipErrorInvalidValue;
+  const int64_t n16 = bytes / 16;
+  const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(n16, 256 * 4), 256 * 16);
+  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, s, buf, n16, out);
   return hipGetLastError();
 }
 

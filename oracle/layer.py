@@ -18,11 +18,17 @@ RMSNorm: y = sum shared + sum p_i E_i(x) with experts at width d.
 
 Readings where the pages leave a step open (each also listed in the design notes):
 * Expert network: a SwiGLU GLU, h = SiLU(W_gate z) * (W_up_e z), o = W_down_e h
-  ("one routed expert: a GLU holds three matrices: gate, up, down").
+  (each routed expert is a GLU with gate, up and down matrices; lesson 6, "Deriving the
+  headline number").
 * Router input is the full-width x (eq. 13 writes W_r x).
 * Top-k order: descending key, equal keys -> lower expert id first.
 * RMSNorm: n = gamma * u / sqrt(mean(u^2) + eps).
 * Shared experts take the raw x and are the same GLU at width d.
+* BF16 LoRA deltas ("Serving K3, 01 architecture", the paragraph on the MXFP4 KL floor: fine-tuning
+  ships BF16 LoRA deltas over the MXFP4 base weights): when the shape has lora_rank r > 0, every
+  routed expert matrix W [N, K] (gate, up, down) is W + B A with bf16 A [r, K] and B [N, r]; the
+  product is exact in fp64, so the delta is taken as B (A v) on the activation v the base matrix
+  sees. Shared experts and the dense projections carry no deltas.
 * Quantisation points (the workload's definition): x arrives as bf16; the
   latent z fed to the experts and the GLU hidden h are rounded to bf16
   ("bf16" workloads) or MX-encoded as MXFP8 in blocks of 32 along the feature
@@ -137,14 +143,34 @@ def routing_tables(idx, E: int):
 # experts
 # ----------------------------------------------------------------------------------------------
 
-def glu(zq, G, U, D, act: str):
-    """One GLU expert on a batch of rows: h = Q(SiLU(zq G^T) * (zq U^T)), o = h D^T.
+def with_delta(v, W, ab=None):
+    """v W^T, plus the LoRA delta (v A^T) B^T when ab = (A, B) is given: v (W + B A)^T."""
+    out = v @ W.T
+    if ab is not None:
+        A, B = ab
+        out = out + (v @ A.T) @ B.T
+    return out
+
+
+def glu(zq, G, U, D, act: str, lora=None):
+    """One GLU expert on a batch of rows: h = Q(SiLU(zq G^T) * (zq U^T)), o = h D^T, each matrix with
+    its LoRA delta when `lora` (dict of fp64 factors a_gate, b_gate, a_up, b_up, a_down, b_down) is given.
     Returns (o, hq, h pre-quantisation, h codes, h scales)."""
-    g = zq @ G.T
-    v = zq @ U.T
+    lg = (lora["a_gate"], lora["b_gate"]) if lora else None
+    lu = (lora["a_up"], lora["b_up"]) if lora else None
+    ld = (lora["a_down"], lora["b_down"]) if lora else None
+    g = with_delta(zq, G, lg)
+    v = with_delta(zq, U, lu)
     hpre = silu(g) * v
     hq, hc, hs = q_act(hpre, act)
-    return hq @ D.T, hq, hpre, hc, hs
+    return with_delta(hq, D, ld), hq, hpre, hc, hs
+
+
+def lora_factors(weights, e, shape):
+    """fp64 LoRA factors of routed expert e (bf16 values, exact), or None without deltas."""
+    if not getattr(shape, "lora_rank", 0):
+        return None
+    return {k: mx.bf16_from_bits(v) for k, v in weights.lora(e).items()}
 
 
 def dequant(mxpair):
@@ -214,10 +240,11 @@ def forward(x_bits, weights, shape, select_override=None, keep_expert_rows=True,
         r0, r1 = offsets[e], offsets[e + 1]
         (gc, uc, dc) = weights.routed(int(e))
         G, U, D = dequant(_first(gc)), dequant(_first(uc)), dequant(_first(dc))
-        o, hq, hpre, _, _ = glu(zq[perm[r0:r1]], G, U, D, s_.act)
+        lo = lora_factors(weights, int(e), s_)
+        o, hq, hpre, _, _ = glu(zq[perm[r0:r1]], G, U, D, s_.act, lo)
         if h_override is not None:
             hq = np.asarray(h_override, np.float64)[row_tj[r0:r1, 0], row_tj[r0:r1, 1]]
-            o = hq @ D.T
+            o = with_delta(hq, D, (lo["a_down"], lo["b_down"]) if lo else None)
         rows_out[r0:r1] = o
         if keep_expert_rows:
             rows_h[r0:r1] = hq
@@ -248,6 +275,26 @@ def forward(x_bits, weights, shape, select_override=None, keep_expert_rows=True,
     taps.update(y_shared=y_shared, hs=hs_list, y_routed=y_routed)
 
     return Result(y=y_shared + y_routed, taps=taps)
+
+
+# ----------------------------------------------------------------------------------------------
+# expert-parallel send side ("Serving K3, 01 architecture": experts sharded over accelerators, an
+# all-to-all of data-dependent sizes; "Kimi K3: architectural innovations", "Compress the expert
+# interface": what crosses is the latent). Experts in n_ranks contiguous ranges of E / n_ranks.
+# ----------------------------------------------------------------------------------------------
+
+def ep_send_counts(idx, E: int, n_ranks: int):
+    """Rows each rank receives: the number of (token, slot) pairs whose expert lies in its range."""
+    assert E % n_ranks == 0
+    per = E // n_ranks
+    dest = np.asarray(idx, np.int64).reshape(-1) // per
+    return np.bincount(dest, minlength=n_ranks).astype(np.int64)
+
+
+def ep_send_rows(routed_in, perm):
+    """The send buffer: the routed input (z after its quantisation point, or x at full width) of every
+    dispatched row, in dispatched order (expert ascending, token ascending) -- grouped by destination."""
+    return np.asarray(routed_in)[np.asarray(perm, np.int64)]
 
 
 def _first(pair):

@@ -77,6 +77,43 @@ def check_mx_quant(gpu_codes, gpu_scales, gpu_pre, oracle_pre, bound, fmt="e4m3"
     return int(((c3 != gpu_codes) | np.repeat(s3 != gpu_scales, 32, axis=-1)).sum())
 
 
+# The scaled MFMA (MXFP8 x MXFP4, 128-wide K windows) accumulates each window's products with an error
+# measured at about 2^-16 of the window's sum of magnitudes (reading R26); doubled, and summed over the
+# windows, that is 2^-15 of the whole sum of magnitudes.
+SCALED_MFMA_REL = 2.0 ** -15
+
+
+def glu_hidden_bound(zr, G, U, lo=None, scaled_mfma=False):
+    """Exact fp64 GLU hidden SiLU(zr G'^T) * (zr U'^T) of some rows (G', U' the matrices with their LoRA
+    deltas when `lo` is given) and a bound on an fp32 implementation's error in it: the dot-product
+    bound of each product (with the LoRA factor's magnitudes added to the weights', and a second
+    accumulation of rank terms; with `scaled_mfma`, plus the scaled MFMA's window term), propagated
+    through SiLU (|SiLU'| <= 1.1) and the product, plus 16 fp32 roundings of the result for the
+    SiLU's exponential, reciprocal and products."""
+    az = np.abs(zr)
+    K = zr.shape[1]
+
+    def prod(W, a, b):
+        mag = az @ np.abs(W).T
+        if lo is None:
+            return zr @ W.T, dot_error_bound(az, np.abs(W)) + (SCALED_MFMA_REL * mag if scaled_mfma else 0.0)
+        A, B = lo[a], lo[b]
+        t = zr @ A.T
+        val = zr @ W.T + t @ B.T
+        bnd = 8.0 * np.sqrt(K) * U32 * (az @ (np.abs(W) + np.abs(B) @ np.abs(A)).T)
+        bnd += 8.0 * np.sqrt(A.shape[0]) * U32 * (np.abs(t) @ np.abs(B).T) + 1e-30
+        if scaled_mfma:
+            bnd += SCALED_MFMA_REL * mag
+        return val, bnd
+
+    g, bg = prod(G, "a_gate", "b_gate")
+    v, bv = prod(U, "a_up", "b_up")
+    sg = layer.silu(g)
+    h = sg * v
+    bound = 1.1 * bg * (np.abs(v) + bv) + (np.abs(sg) + 1.1 * bg) * bv + 16.0 * U32 * np.abs(h) + 1e-30
+    return h, bound
+
+
 def check_routing(gpu, sel, E):
     """Selection within key ties, and dispatch tables bit-exact for the GPU's selection."""
     idx = gpu["topk_idx"].astype(np.int64)
@@ -116,9 +153,12 @@ def stagewise(g, weights, shape, x_bits):
     for e in np.nonzero(g["counts"])[0]:
         r0, r1 = offsets[e], offsets[e + 1]
         G, U, D = (layer.dequant(m) for m in _first3(weights.routed(int(e))))
+        lo = layer.lora_factors(weights, int(e), s)
         zr = zq[perm[r0:r1]]
-        h_ref[r0:r1] = layer.silu(zr @ G.T) * (zr @ U.T)
-        o_ref[r0:r1] = hq[r0:r1] @ D.T
+        pair = (lambda a, b: (lo[a], lo[b]) if lo else None)  # noqa: E731
+        h_ref[r0:r1] = layer.silu(layer.with_delta(zr, G, pair("a_gate", "b_gate"))) * \
+            layer.with_delta(zr, U, pair("a_up", "b_up"))
+        o_ref[r0:r1] = layer.with_delta(hq[r0:r1], D, pair("a_down", "b_down"))
     out["h"] = rel_l2(g["h_f32"], h_ref)
     out["o"] = rel_l2(g["expert_out"], o_ref)
     inv = g["inv"].reshape(T, s.k)

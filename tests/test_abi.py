@@ -82,3 +82,65 @@ def test_null_ctx_error_text():
     L = k3.lib()
     assert L.k3moe_create(None, None) == k3.EINVAL
     assert L.k3moe_last_error(None)
+
+
+def _c_layout(struct, fields):
+    """sizeof and offsetof of a C struct of include/k3moe.h, from a small C program built with gcc."""
+    import shutil
+    import subprocess
+    import tempfile
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    lines = [f'  printf("size %zu\\n", sizeof({struct}));']
+    lines += [f'  printf("{f} %zu\\n", offsetof({struct}, {f}));' for f in fields]
+    src = "#include <stddef.h>\n#include <stdio.h>\n#include \"k3moe.h\"\nint main(void) {\n" + "\n".join(lines) + \
+          "\n  return 0;\n}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), c, "-o", exe],
+                       check=True, capture_output=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout
+    return {k: int(v) for k, v in (line.split() for line in out.splitlines())}
+
+
+@pytest.mark.parametrize("struct,cls", [("k3moe_config", "Config"), ("k3moe_mx", "MX"), ("k3moe_lora", "Lora"),
+                                        ("k3moe_weights", "Weights"), ("k3moe_taps", "Taps")])
+def test_struct_layout_matches_header(struct, cls):
+    """The binding's ctypes mirrors of the header's structs: every field at the C offset, same size."""
+    C = getattr(k3, cls)
+    fields = [f for f, _ in C._fields_]
+    lay = _c_layout(struct, fields)
+    assert lay["size"] == ctypes.sizeof(C), (struct, lay["size"], ctypes.sizeof(C))
+    for f in fields:
+        assert lay[f] == getattr(C, f).offset, (struct, f, lay[f], getattr(C, f).offset)
+
+
+def test_new_entry_points_check_arguments_before_any_device_work():
+    m = k3.K3MoE(_cfg(lora_rank=16))
+    L = k3.lib()
+    # expert-parallel split: state and argument errors
+    assert L.k3moe_forward_head(m._h, None, 4, None, None, 3, None, None, None, None) == k3.EINVAL
+    assert "divide" in m.last_error()
+    assert L.k3moe_forward_head(m._h, None, 4, None, None, 4, None, None, None, None) == k3.ESTATE
+    assert L.k3moe_experts_forward(m._h, None, None, 4 * 64 + 1, None, None, None, None) == k3.ETOOBIG
+    assert L.k3moe_experts_forward(m._h, None, None, 8, None, None, None, None) == k3.ESTATE
+    assert L.k3moe_forward_tail(m._h, None, 4, None, None, None) == k3.ESTATE
+    assert L.k3moe_forward_tail(m._h, None, 65, None, None, None) == k3.ETOOBIG
+    # LoRA factors are required when the rank is set
+    w = k3.Weights()
+    w.routed_first, w.routed_count = 0, 1
+    mx1 = (k3.MX * 1)(k3.MX(256, 256))
+    w.gate = w.up = w.down = ctypes.cast(mx1, ctypes.POINTER(k3.MX))
+    assert L.k3moe_pack_weights(m._h, ctypes.byref(w), 256, None) == k3.EINVAL
+    assert "LoRA" in m.last_error()
+    # measurement aid
+    assert L.k3moe_stream_read(None, 16, None, None) == k3.EINVAL
+    assert L.k3moe_stream_read(256, 17, 256, None) == k3.EINVAL
+
+
+@pytest.mark.parametrize("rank", [4, 33, -8])
+def test_create_rejects_bad_lora_rank(rank):
+    with pytest.raises(k3.K3MoEError):
+        k3.K3MoE(_cfg(lora_rank=rank))

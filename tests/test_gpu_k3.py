@@ -4,8 +4,13 @@ the launch configuration the benchmark times.
 Every token: router scores, selection (exact up to oracle key ties < 1e-6, counted), p, counts,
 offsets, permutation and inverse (bit-exact), and the latent z at its quantisation point (bf16
 or MXFP8 codes: strict against the oracle's encoder on the GPU's fp32 values, end to end
-against the oracle's own values). Sampled tokens: y, u, n and the shared hidden against the
-oracle's per-token forward. One packed layer is resident at a time.
+against the oracle's own values, boundary codes counted).
+Outputs: the decode batch of 64 tokens whole (y, u, n and the shared hidden of every token against
+the oracle's forward); the skewed and full-width batches on 16 tokens spread through the batch; the
+prefill chunk stage-wise on every dispatched row of 64 experts spread over the id range (the
+hottest, ids above 512, a count that is not a multiple of the 192-row chunk) and end to end on 64
+tokens spread through the batch. Also the BF16 LoRA variant at decode and the expert-parallel split
+(one rank's 112 experts on its rows) at decode and prefill. One packed layer is resident at a time.
 """
 from __future__ import annotations
 
@@ -36,6 +41,7 @@ def get_layer(wl, max_tokens):
     key = (wl.seed, wl.shape, max_tokens)
     if _CUR["key"] != key:
         _CUR["moe"] = None
+        _CUR.pop("rank", None)
         gc.collect()
         torch.cuda.empty_cache()
         _log(f"[k3] packing seed {wl.seed} {wl.shape}")
@@ -49,7 +55,7 @@ def get_layer(wl, max_tokens):
     return _CUR["moe"]
 
 
-def run_taps(moe, wl, T):
+def run_taps(moe, wl, T, rows=False):
     s = wl.shape
     f8 = s.act == "mxfp8"
     dev = "cuda"
@@ -69,20 +75,32 @@ def run_taps(moe, wl, T):
             t["z_scales"] = torch.empty(T, s.l // 32, dtype=torch.uint8, device=dev)
     if s.Ns:
         t["hs"] = torch.empty(T, s.Ns * s.hs, dtype=torch.bfloat16, device=dev)
+    if rows:
+        t.update(h=torch.empty(T * s.k, s.h, dtype=torch.uint8 if f8 else torch.bfloat16, device=dev),
+                 h_f32=torch.empty(T * s.k, s.h, dtype=torch.float32, device=dev),
+                 expert_out=torch.empty(T * s.k, s.expert_in, dtype=torch.float32, device=dev))
+        if f8:
+            t["h_scales"] = torch.empty(T * s.k, s.h // 32, dtype=torch.uint8, device=dev)
     x = wdev.x_tensor(wl, T)
     y = moe.forward(x, taps=t)
     torch.cuda.synchronize()
     g = {k: (parity.bf16_bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in t.items()}
+    del t
     g["y"] = parity.np64(y)
     return g
 
 
-def check_layer(wl, sample, max_tokens=None):
+def spread(T, n, extra=()):
+    """n token indices spread evenly through [0, T), plus some chosen ones."""
+    return sorted(set(np.linspace(0, T - 1, n).round().astype(int).tolist()) | set(extra))
+
+
+def check_layer(wl, sample, max_tokens=None, rows=False):
     s = wl.shape
     T = wl.T
     moe = get_layer(wl, max_tokens or T)
     _log(f"[k3] {wl.name}: GPU forward T={T}")
-    g = run_taps(moe, wl, T)
+    g = run_taps(moe, wl, T, rows=rows)
     xb = wl.x_bits()
     xh = mx.bf16_from_bits(xb)
     # router over every token
@@ -95,7 +113,8 @@ def check_layer(wl, sample, max_tokens=None):
     counts = g["counts"]
     _log(f"[k3] {wl.name}: routing ok, flips {flips}, active experts {(counts > 0).sum()}, "
          f"max/mean load {counts.max() / counts.mean():.2f}")
-    # latent z of every token at its quantisation point
+    # latent z of every token at its quantisation point; tokens with a boundary code marked
+    zdirty = np.zeros(T, bool)
     if s.latent_moe:
         Wd = layer.dequant(wl.w_down())
         aWd = np.abs(Wd)
@@ -104,42 +123,118 @@ def check_layer(wl, sample, max_tokens=None):
             xs = xh[r0:r0 + 1024]
             z = xs @ Wd.T
             bound = parity.dot_error_bound(np.abs(xs), aWd)
+            sl = slice(r0, r0 + 1024)
             if s.act == "mxfp8":
-                nz += parity.check_mx_quant(g["z"][r0:r0 + 1024], g["z_scales"][r0:r0 + 1024],
-                                            g["z_f32"][r0:r0 + 1024], z, bound)
+                nz += parity.check_mx_quant(g["z"][sl], g["z_scales"][sl], g["z_f32"][sl], z, bound)
+                c3, s3 = mx.mx_quantize(z, "e4m3")
+                zdirty[sl] = (c3 != g["z"][sl]).any(axis=1) | (s3 != g["z_scales"][sl]).any(axis=1)
             else:
-                nz += parity.check_bf16_quant(g["z"][r0:r0 + 1024], g["z_f32"][r0:r0 + 1024], z, bound)
+                nz += parity.check_bf16_quant(g["z"][sl], g["z_f32"][sl], z, bound)
+                zdirty[sl] = (mx.bf16_round(z) != mx.bf16_from_bits(g["z"][sl])).any(axis=1)
         assert nz <= 1e-3 * T * s.l + 2
-        _log(f"[k3] {wl.name}: z quantisation ok ({nz} boundary cases)")
-    # sampled tokens through the whole layer
+        _log(f"[k3] {wl.name}: z quantisation ok ({nz} boundary codes in {int(zdirty.sum())} tokens)")
+    # sampled tokens through the whole layer: against the oracle's own chain (full bar; selection of
+    # flipped tokens taken from the GPU), and for MXFP8 also against the oracle taking the GPU's codes
     ov = {i: gidx[t] for i, t in enumerate(sample)}
+    _log(f"[k3] {wl.name}: oracle forward on {len(sample)} tokens")
     ref = layer.forward(xb[sample], wl, s, select_override=ov, keep_expert_rows=False)
-    rel, ma = parity.assert_y(g["y"][sample], ref.y, "y")
-    parity.assert_y(g["u"][sample], ref.taps["u"], "u")
+    clean = np.array([not zdirty[t] for t in sample])
+    if s.act == "mxfp8":
+        # tokens whose z codes all equal the oracle's: the full bar against the oracle's own chain; the
+        # others (a code across a rounding boundary inside the fp32 bound): the full bar against the
+        # oracle taking the GPU's z and h codes
+        assert clean.sum() >= min(8, len(sample)), f"{clean.sum()} clean tokens"
+        rel, ma = parity.assert_y(g["y"][sample][clean], ref.y[clean], "y (clean tokens)")
+        dirty = [t for t in sample if zdirty[t]]
+        if rows and dirty:
+            rsel = g["inv"].reshape(T, s.k)[dirty]                      # [n, k] dispatched rows
+            hq = parity.decode_act(g["h"][rsel.reshape(-1)], g["h_scales"][rsel.reshape(-1)], "mxfp8")
+            zq = parity.decode_act(g["z"][dirty], g["z_scales"][dirty], "mxfp8")
+            ovd = {i: gidx[t] for i, t in enumerate(dirty)}
+            refq = layer.forward(xb[dirty], wl, s, select_override=ovd, keep_expert_rows=False, z_override=zq,
+                                 h_override=hq.reshape(len(dirty), s.k, s.h))
+            rq, mq = parity.assert_y(g["y"][dirty], refq.y, "y (oracle on the GPU's codes)")
+            _log(f"[k3] {wl.name}: {len(dirty)} tokens with a boundary z code vs oracle on the GPU's codes: "
+                 f"rel L2 {rq:.2e}, max-abs/rms {mq:.2e}")
+    else:
+        rel, ma = parity.assert_y(g["y"][sample], ref.y, "y")
+    parity.assert_y(g["u"][sample][clean], ref.taps["u"][clean], "u")
     if s.latent_moe:
-        parity.assert_y(mx.bf16_from_bits(g["n"][sample]), ref.taps["n"], "n")
+        parity.assert_y(mx.bf16_from_bits(g["n"][sample][clean]), ref.taps["n"][clean], "n")
     if s.Ns:
         parity.assert_y(mx.bf16_from_bits(g["hs"][sample]), np.concatenate(ref.taps["hs"], axis=1), "shared")
-    _log(f"[k3] {wl.name}: sampled tokens {list(sample)}: y rel L2 {rel:.2e}, max-abs/rms {ma:.2e}")
+    _log(f"[k3] {wl.name}: {len(sample)} sampled tokens ({int(clean.sum())} without a boundary code): "
+         f"y rel L2 {rel:.2e}, max-abs/rms {ma:.2e}")
     return g
 
 
+def stagewise_experts(wl, g, experts):
+    """Every dispatched row of the given experts: the gate/up + SwiGLU values against the oracle's step
+    on the GPU's own quantised latent (element-wise within the fp32 bound), and the down projection
+    against the oracle on the GPU's own quantised hidden (relative L2 <= 1e-4, R26)."""
+    s = wl.shape
+    perm, offsets = g["perm"].astype(np.int64), g["offsets"]
+    zq = parity.decode_act(g["z"], g.get("z_scales"), s.act)
+    worst_h, worst_o, rows = 0.0, 0.0, 0
+    for e in experts:
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 == r0:
+            continue
+        G, U, D = (layer.dequant(m) for m in parity._first3(wl.routed(int(e))))
+        h_ex, hb = parity.glu_hidden_bound(zq[perm[r0:r1]], G, U, layer.lora_factors(wl, int(e), s),
+                                           scaled_mfma=s.act == "mxfp8")
+        err = np.abs(g["h_f32"][r0:r1] - h_ex)
+        worst_h = max(worst_h, float(np.max(err / hb)))
+        assert np.all(err <= hb), f"expert {e}: hidden off by {np.max(err / hb):.3g} x the bound"
+        hq = parity.decode_act(g["h"][r0:r1], g["h_scales"][r0:r1] if "h_scales" in g else None, s.act)
+        o_ref = hq @ D.T
+        rel = parity.rel_l2(g["expert_out"][r0:r1], o_ref)
+        worst_o = max(worst_o, rel)
+        assert rel < 1e-4, (e, rel)
+        rows += r1 - r0
+    return worst_h, worst_o, rows
+
+
 @pytest.mark.timeout(900)
-def test_k3_decode_t64():
-    check_layer(workloads.get("k3_decode_t64"), [0, 21, 63], max_tokens=512)
+def test_k3_decode_t64_every_token():
+    """The decode batch whole: every token's y, u, n and shared hidden against the oracle."""
+    wl = workloads.get("k3_decode_t64")
+    check_layer(wl, list(range(64)), max_tokens=512)
+
+
+@pytest.mark.timeout(900)
+def test_k3_expert_parallel_rank_decode():
+    _rank_check(workloads.get("k3_decode_t64"), rank=3)
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["k3_decode_t512_zipf", "k3_decode_t512_zipf_cal"])
 def test_k3_decode_t512_skewed(name):
-    g = check_layer(workloads.get(name), [5, 511], max_tokens=512)
+    g = check_layer(workloads.get(name), spread(512, 16, extra=(5,)), max_tokens=512)
     c = g["counts"]
     assert c.sum() == 512 * 16
 
 
 @pytest.mark.timeout(900)
 def test_k3_prefill_t8192_mxfp8():
-    check_layer(workloads.get("k3_prefill_t8192"), [0, 8191])
+    """Prefill chunk: every row of 64 experts spread over the id range stage-wise; 64 spread tokens
+    end to end."""
+    wl = workloads.get("k3_prefill_t8192")
+    g = check_layer(wl, spread(8192, 64), rows=True)
+    c = g["counts"]
+    hot = int(np.argmax(c))
+    ragged = [int(e) for e in np.nonzero(c % 192 != 0)[0] if e >= 512][:4]
+    experts = sorted(set(np.linspace(0, 895, 56).round().astype(int).tolist()) | {hot} | set(ragged) |
+                     set(range(512, 516)))
+    assert len(experts) >= 64
+    wh, wo, rows = stagewise_experts(wl, g, experts)
+    _log(f"[k3] prefill stage-wise: {len(experts)} experts (hottest {hot} with {c[hot]} rows), {rows} rows: "
+         f"hidden within {wh:.3f} x its bound, expert outputs rel L2 <= {wo:.2e}")
+
+
+@pytest.mark.timeout(900)
+def test_k3_expert_parallel_rank_prefill():
+    _rank_check(workloads.get("k3_prefill_t8192"), rank=5)
 
 
 @pytest.mark.timeout(900)
@@ -156,14 +251,68 @@ def test_k3_decode_repeat_bit_identical():
     assert torch.equal(perm[0], perm[1])
 
 
+def _rank_check(wl, rank, n_ranks=8):
+    """One expert-parallel rank: its 112 experts on a context of their own, run on the rows the head
+    sends it, reproduce the full layer's expert outputs for those rows bit for bit (same kernels on the
+    same rows), and the send side matches the oracle (counts exactly, rows bit for bit)."""
+    s = wl.shape
+    T = wl.T
+    full = get_layer(wl, T if T > 64 else 512)
+    per = s.E // n_ranks
+    key = ("rank", wl.seed, s, rank)
+    if _CUR.get("rank", (None,))[0] != key:
+        _CUR.pop("rank", None)
+        gc.collect()
+        _log(f"[k3] packing rank {rank} of {n_ranks}: experts {rank * per}..{(rank + 1) * per - 1}")
+        _CUR["rank"] = (key, wdev.build_layer(wl, s, max_tokens=T, experts=range(rank * per, (rank + 1) * per),
+                                              dense=False))
+    loc = _CUR["rank"][1]
+    x = wdev.x_tensor(wl)
+    taps = {"expert_out": torch.empty(T * s.k, s.l, dtype=torch.float32, device="cuda"),
+            "perm": torch.empty(T * s.k, dtype=torch.int32, device="cuda"),
+            "topk_idx": torch.empty(T, s.k, dtype=torch.int32, device="cuda")}
+    if s.act == "mxfp8":
+        taps.update(z=torch.empty(T, s.l, dtype=torch.uint8, device="cuda"),
+                    z_scales=torch.empty(T, s.l // 32, dtype=torch.uint8, device="cuda"))
+    else:
+        taps["z"] = torch.empty(T, s.l, dtype=torch.bfloat16, device="cuda")
+    full.forward(x, taps=taps)
+    rows, scales, send, counts = full.forward_head(x, n_ranks)
+    torch.cuda.synchronize()
+    idx = taps["topk_idx"].cpu().numpy()
+    send_np = send.cpu().numpy()
+    assert send_np.tolist() == layer.ep_send_counts(idx, s.E, n_ranks).tolist()
+    perm = taps["perm"].cpu().long()
+    if s.act == "mxfp8":
+        assert torch.equal(rows.cpu(), taps["z"].cpu()[perm]) and torch.equal(scales.cpu(), taps["z_scales"].cpu()[perm])
+    else:
+        assert torch.equal(rows.view(torch.int16).cpu(), taps["z"].view(torch.int16).cpu()[perm])
+    start = int(send_np[:rank].sum())
+    R = int(send_np[rank])
+    sl = slice(start, start + R)
+    out = loc.experts_forward(rows[sl], scales[sl] if scales is not None else None,
+                              counts[rank * per:(rank + 1) * per].contiguous())
+    torch.cuda.synchronize()
+    same = torch.equal(out.view(torch.int32).cpu(), taps["expert_out"][sl].view(torch.int32).cpu())
+    assert same, "rank outputs differ from the full layer's"
+    _log(f"[k3] {wl.name}: rank {rank}/{n_ranks}: {R} rows over {per} experts "
+         f"({int((counts[rank * per:(rank + 1) * per] > 0).sum())} active): bit-identical to the full layer")
+
+
 @pytest.mark.timeout(900)
 def test_k3_t2048_bf16():
     """K3 shape, 2048 tokens, bf16 activations: every expert on the row-tiled grouped bf16 kernel."""
-    check_layer(workloads.get("k3_t2048"), [0, 1000, 2047])
+    check_layer(workloads.get("k3_t2048"), spread(2048, 16))
+
+
+@pytest.mark.timeout(900)
+def test_k3_decode_t64_lora():
+    """Rank-16 BF16 LoRA deltas on every routed expert matrix, decode batch: 16 spread tokens."""
+    check_layer(workloads.get("k3_decode_t64_lora"), spread(64, 16))
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("T", [64, 2048])
 def test_fullwidth(T):
     wl = workloads.get("fullwidth_t2048").with_tokens(T)
-    check_layer(wl, [0, T - 1], max_tokens=2048)
+    check_layer(wl, spread(T, 16), max_tokens=2048)

@@ -90,50 +90,88 @@ def check_all(name, T):
         ref = layer.forward(wl.x_bits(T), w, s, select_override={t: gidx[t] for t in range(T)})
         rt = ref.taps
     f8 = s.act == "mxfp8"
-    # latent z at its quantisation point
+    perm = g["perm"].astype(np.int64)
+    # latent z at its quantisation point: strict encoding of the GPU's own values, the values within
+    # the fp32 accumulation bound of the oracle's, and the tokens whose codes differ from the oracle's
+    # own encoding (a rounding boundary inside that bound) marked
+    zdirty = np.zeros(T, bool)
     if s.latent_moe:
         xh = mx.bf16_from_bits(wl.x_bits(T))
         bound = parity.dot_error_bound(np.abs(xh), np.abs(layer.dequant(w.w_down())))
         if f8:
             nz = parity.check_mx_quant(g["z"], g["z_scales"], g["z_f32"], rt["z"], bound)
+            zdirty = (parity.decode_act(g["z"], g["z_scales"], "mxfp8") != rt["zq"]).any(axis=1)
         else:
             nz = parity.check_bf16_quant(g["z"], g["z_f32"], rt["z"], bound)
+            zdirty = (mx.bf16_from_bits(g["z"]) != rt["zq"]).any(axis=1)
         assert nz <= max(2, 1e-3 * g["z_f32"].size)
-    # GLU hidden (dispatched row order): strict quantisation of the GPU's own values, and the
-    # GPU pre-quantisation values close to the oracle's
+    # GLU hidden (dispatched row order): strict quantisation of the GPU's own values; on the rows of
+    # tokens whose z equals the oracle's, the GPU's values within the fp32 bound of the oracle's and
+    # the codes that differ from the oracle's own encoding counted (boundary cases inside the bound)
     if f8:
         c2, s2 = mx.mx_quantize(g["h_f32"].astype(np.float64), "e4m3")
         assert np.array_equal(c2, g["h"]) and np.array_equal(s2, g["h_scales"])
     else:
         assert np.array_equal(mx.bf16_round(g["h_f32"].astype(np.float64)), mx.bf16_from_bits(g["h"]))
+    hq_gpu = parity.decode_act(g["h"], g.get("h_scales"), s.act)
+    zq_ref = rt["zq"] if s.latent_moe else mx.bf16_from_bits(wl.x_bits(T))
+    clean_rows = ~zdirty[perm]
+    hdirty_rows = np.zeros(T * s.k, bool)
+    nh_el, n_el = 0, 0
+    offsets = g["offsets"]
+    for e in np.nonzero(g["counts"])[0]:
+        r0, r1 = offsets[e], offsets[e + 1]
+        rows = np.arange(r0, r1)[clean_rows[r0:r1]]
+        if rows.size == 0:
+            continue
+        G, U, _ = (layer.dequant(m) for m in w.experts[e])
+        h_ex, hb = parity.glu_hidden_bound(zq_ref[perm[rows]], G, U, layer.lora_factors(w, int(e), s),
+                                           scaled_mfma=f8)
+        err = np.abs(g["h_f32"][rows] - h_ex)
+        assert np.all(err <= hb), f"expert {e}: hidden off by {np.max(err / hb):.3g} x the bound"
+        diff = hq_gpu[rows] != rt["h"][rows]
+        hdirty_rows[rows] = diff.any(axis=1)
+        nh_el += int(diff.sum())
+        n_el += diff.size
+    nh = int(hdirty_rows.sum())
+    # each differing code is a value within the bound above on the other side of a rounding boundary
+    # (the encoder is checked strictly on the GPU's own values); they are rare among the elements
+    assert nh_el <= max(2, 1e-3 * n_el), (nh_el, n_el)
+    dirty = zdirty.copy()
+    dirty[perm[hdirty_rows]] = True
+    clean = ~dirty
     # each routed-path kernel against the oracle's step on the GPU's own (quantised) inputs
     sw = parity.stagewise(g, w, s, wl.x_bits(T))
-    # and end to end against the oracle's own chain (loose: MXFP8 codes on the other side of a
-    # rounding boundary move single elements by one E4M3 step)
-    rel_h = parity.rel_l2(g["h_f32"], rt["hpre"])
-    assert rel_h < (3e-2 if f8 else 2e-3), rel_h
-    rel_u = parity.rel_l2(g["u"], rt["u"])
-    assert rel_u < (2e-2 if f8 else 5e-3), rel_u
     if s.Ns:
         parity.assert_y(mx.bf16_from_bits(g["hs"]), np.concatenate(rt["hs"], axis=1), "shared hidden")
-    # the bar on y: against the oracle whose quantisation decisions are taken on the GPU's values
-    # (z and h after their quantisation points, strict-checked above against the oracle's encoder)
+    # the bar on y, every token: against the oracle whose quantisation decisions are taken on the GPU's
+    # values (z and h after their quantisation points, strict-checked above against the oracle's encoder)
     zq_g = parity.decode_act(g["z"], g.get("z_scales"), s.act) if s.latent_moe else None
-    hq_g = parity.decode_act(g["h"], g.get("h_scales"), s.act)[g["inv"].reshape(T, s.k)]
+    hq_g = hq_gpu[g["inv"].reshape(T, s.k)]
     ref_q = layer.forward(wl.x_bits(T), w, s, select_override={t: gidx[t] for t in range(T)},
                           z_override=zq_g, h_override=hq_g)
     rel, ma = parity.assert_y(g["y"], ref_q.y)
-    # and end to end against the oracle's own chain (bf16: the same bar; MXFP8: codes across a
-    # rounding boundary move single elements by one E4M3 step, so only the L2 part of the bar)
-    rel_e, ma_e = parity.y_metrics(g["y"], ref.y)
-    assert rel_e <= parity.Y_REL_L2 and (f8 or ma_e <= parity.Y_MAXABS_RMS), (rel_e, ma_e)
-    _log(f"[check] {name} T={T}: flips {flips} rel_l2 {rel:.2e} maxabs/rms {ma:.2e} stagewise {sw}")
+    # and the same bar against the oracle's own chain on every token whose quantised activations all
+    # equal the oracle's (most tokens; the rest differ by a code across a rounding boundary)
+    # (the boundary codes themselves are bounded per element above; with wide rows a token often holds one)
+    assert clean.sum() >= min(T // 8, 16), f"only {clean.sum()} of {T} tokens without a boundary code"
+    rel_c, ma_c = float("nan"), float("nan")
+    if clean.any():
+        rel_c, ma_c = parity.assert_y(g["y"][clean], ref.y[clean], "y (oracle chain, clean tokens)")
+        parity.assert_y(g["u"][clean], rt["u"][clean], "u (oracle chain, clean tokens)")
+    if not f8:
+        parity.assert_y(g["y"], ref.y, "y (oracle chain, every token)")
+    _log(f"[check] {name} T={T}: flips {flips}, boundary codes z {int(zdirty.sum())} tokens / h {nh} rows "
+         f"({nh_el} of {n_el} elements), "
+         f"clean tokens {int(clean.sum())}/{T}; y vs oracle(GPU codes) rel_l2 {rel:.2e} maxabs/rms {ma:.2e}; "
+         f"clean tokens vs oracle rel_l2 {rel_c:.2e} maxabs/rms {ma_c:.2e}; stagewise {sw}")
     return g
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_mxfp8", "tiny_mxfp8_many", "tiny_mxfp8_deep", "tiny_dense_many",
                                   "tiny_fullwidth", "tiny_skewed", "tiny_bf16_many", "tiny_bf16_deep", "tiny_split",
-                                  "tiny_split_mxfp8", "tiny_e12_mxfp8", "tiny_e4_bf16"])
+                                  "tiny_split_mxfp8", "tiny_e12_mxfp8", "tiny_e4_bf16", "tiny_lora",
+                                  "tiny_lora_mxfp8_many", "tiny_lora_bf16_many", "tiny_lora_split"])
 def test_full_parity(name):
     check_all(name, workloads.get(name).T)
 

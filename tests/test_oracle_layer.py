@@ -322,3 +322,94 @@ def test_generator_weights_are_oracle_mx_encoding():
     c2, s2 = mx.mx_quantize(vals, "e2m1")
     assert np.array_equal(scales, s2)
     assert np.array_equal(mx.unpack_fp4(codes), c2)
+
+
+# ---------------------------------------------------------------------------------------------
+# the override path (activations after their quantisation points supplied from outside)
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+def test_override_with_own_quantised_values_is_identity(tiny_w, tiny_x, act):
+    """z_override / h_override fed with the oracle's own quantised z and hidden (the hidden given per
+    (token, selection slot)) reproduce the oracle's own output bit for bit."""
+    shape = replace(TINY.shape, act=act)
+    r = layer.forward(tiny_x, tiny_w, shape)
+    h_tk = r.taps["h"][r.taps["inv"]]                       # dispatched rows -> [T, k, h]
+    r2 = layer.forward(tiny_x, tiny_w, shape, z_override=r.taps["zq"], h_override=h_tk)
+    assert np.array_equal(r2.y, r.y)
+    assert np.array_equal(r2.taps["expert_out"], r.taps["expert_out"])
+    assert np.array_equal(r2.taps["u"], r.taps["u"])
+
+
+@pytest.mark.parametrize("t,j", [(0, 0), (3, 1), (17, 3), (63, 2)])
+def test_override_hidden_lands_on_its_token_and_slot(tiny_w, tiny_x, t, j):
+    """A one-hot hidden at (token t, slot j) and zeros elsewhere: the combine gives u_t = p_tj times
+    column m of the down-projection of expert idx[t, j] (eq. 11), and u = 0 for every other token.
+    Fixes the dispatched-row <-> (token, slot) mapping of the override path by construction."""
+    s = TINY.shape
+    r = layer.forward(tiny_x, tiny_w, s)
+    T = tiny_x.shape[0]
+    m = 5 + 7 * j
+    h = np.zeros((T, s.k, s.h))
+    h[t, j, m] = 1.0
+    r2 = layer.forward(tiny_x, tiny_w, s, z_override=r.taps["zq"], h_override=h)
+    e = r.taps["idx"][t, j]
+    D = layer.dequant(tiny_w.experts[e][2])
+    expect = r.taps["p"][t, j] * D[:, m]
+    assert np.array_equal(r2.taps["u"][t], expect)
+    others = np.arange(T) != t
+    assert np.all(r2.taps["u"][others] == 0)
+
+
+def test_override_z_row_feeds_its_token_only(tiny_w, tiny_x):
+    """Changing the overriding latent of one token changes that token's routed branch only."""
+    s = TINY.shape
+    r = layer.forward(tiny_x, tiny_w, s)
+    zq = r.taps["zq"].copy()
+    zq[9] = zq[10]
+    r2 = layer.forward(tiny_x, tiny_w, s, z_override=zq)
+    keep = np.arange(tiny_x.shape[0]) != 9
+    assert np.array_equal(r2.y[keep], r.y[keep])
+    assert not np.allclose(r2.y[9], r.y[9])
+
+
+# ---------------------------------------------------------------------------------------------
+# where MXFP8 mode quantises (and where it does not)
+# ---------------------------------------------------------------------------------------------
+
+def _mantissa_bits_needed(v):
+    """Fraction bits of each nonzero value beyond its leading one (exact for fp64 inputs)."""
+    a = np.abs(v[v != 0])
+    m, _ = np.frexp(a)                                      # a = m 2^e, m in [0.5, 1)
+    bits = np.zeros(a.shape, np.int64)
+    f = m * 2.0 - 1.0                                       # fraction in [0, 1)
+    for b in range(1, 60):
+        f = f * 2.0
+        one = f >= 1.0
+        f = np.where(one, f - 1.0, f)
+        bits = np.where(f > 0, b + 1, bits)
+    return bits
+
+
+def test_mxfp8_mode_quantises_only_z_and_h(tiny_w, tiny_x):
+    """MXFP8 workloads put MX quantisation at the routed GEMM inputs only (the workload definition:
+    the latent and the hidden fed to the grouped GEMMs). The shared experts' path is the bf16 one
+    unchanged, the RMSNorm output is the bf16 rounding of RMSNorm(u) (torch fp64 reference) on the
+    run's own u, and neither carries values off the bf16 grid nor is restricted to 3 mantissa bits."""
+    s8 = replace(TINY.shape, act="mxfp8")
+    r8 = layer.forward(tiny_x, tiny_w, s8)
+    rb = layer.forward(tiny_x, tiny_w, TINY.shape)
+    # shared path: identical to the bf16 workload's
+    assert all(np.array_equal(a, b) for a, b in zip(r8.taps["hs"], rb.taps["hs"]))
+    assert np.array_equal(r8.taps["y_shared"], rb.taps["y_shared"])
+    # latent before quantisation: the same W_down x; after: its MX encoding, not its bf16 rounding
+    assert np.array_equal(r8.taps["z"], rb.taps["z"])
+    assert not np.array_equal(r8.taps["zq"], rb.taps["zq"])
+    assert _mantissa_bits_needed(r8.taps["zq"]).max() <= 3
+    # n: bf16 rounding of RMSNorm of this run's u
+    ref = F.rms_norm(_t(r8.taps["u"]), (s8.l,), weight=_t(tiny_w.gamma), eps=s8.eps).numpy()
+    assert np.array_equal(r8.taps["n"], mx.bf16_round(ref))
+    assert _mantissa_bits_needed(r8.taps["n"]).max() > 3
+    assert _mantissa_bits_needed(np.concatenate(r8.taps["hs"], axis=1)).max() > 3
+    # the hidden fed to the down-projection: MX values (at most 3 mantissa bits)
+    assert _mantissa_bits_needed(r8.taps["h"]).max() <= 3

@@ -20,6 +20,7 @@ class ArrayWeights:
         self.shared_mats = []
         self.bias = None
         self.gamma = None
+        self.loras = []
         if wl is not None:
             s = wl.shape
             if s.latent_moe:
@@ -31,6 +32,9 @@ class ArrayWeights:
             self.shared_mats = [wl.shared(j) for j in range(s.Ns)]
             self.bias = wl.router_bias()
             self.gamma = wl.rms_gamma()
+            if s.lora_rank:
+                stack = wl.lora(0, s.E)
+                self.loras = [{n: v[e] for n, v in stack.items()} for e in range(s.E)]
 
     def copy(self):
         return copy.deepcopy(self)
@@ -48,6 +52,9 @@ class ArrayWeights:
     def routed(self, e, count=1):
         assert count == 1
         return self.experts[e]
+
+    def lora(self, e):
+        return self.loras[e]
 
     def shared(self, j):
         return self.shared_mats[j]

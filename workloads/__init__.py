@@ -32,6 +32,8 @@ _LIB = os.path.join(_HERE, "libk3gen.so")
 
 # tensor ids of the counter-based streams
 X, W_ROUTER, W_DOWN, W_UP, GATE, UP, DOWN, SH_GATE, SH_UP, SH_DOWN, ZIPF_PERM = range(1, 12)
+LORA_A_GATE, LORA_B_GATE, LORA_A_UP, LORA_B_UP, LORA_A_DOWN, LORA_B_DOWN = range(12, 18)
+LORA_NAMES = ("a_gate", "b_gate", "a_up", "b_up", "a_down", "b_down")
 
 
 def build(force: bool = True) -> str:
@@ -119,6 +121,7 @@ class LayerShape:
     latent_moe: int = 1   # 1: eq. 11 LatentMoE; 0: conventional full-width MoE
     act: str = "bf16"     # activation format of the routed GEMM inputs: "bf16" | "mxfp8"
     eps: float = 1e-6
+    lora_rank: int = 0    # rank of the BF16 LoRA deltas on every routed expert matrix (0: none)
 
     @property
     def expert_in(self) -> int:
@@ -134,6 +137,7 @@ class Workload:
     seed: int
     bias: str = "zero"        # "zero" | "zipf"
     zipf_alpha: float = 1.5   # b_e = alpha * ln(w_e), w_e Zipf(s=1) weight of expert e's rank
+    lora_b_gain: float = 0.25  # standard deviation of a LoRA delta next to the base product (~1)
     note: str = ""
 
     # ---- inputs -----------------------------------------------------------------------------
@@ -178,6 +182,28 @@ class Workload:
         u = mxfp4(self.seed, UP, e0, s.h, li, li ** -0.5, count=count)
         dn = mxfp4(self.seed, DOWN, e0, li, s.h, s.h ** -0.5, count=count)
         return g, u, dn
+
+    def lora(self, e0: int, count: int | None = None):
+        """BF16 LoRA factors of routed expert e0 (or a stack of `count` experts from e0) as bf16 bit
+        patterns: a_gate, a_up [r, l'] ~ N(0, 1/l'); a_down [r, h] ~ N(0, 1/h); b_gate, b_up [h, r] and
+        b_down [l', r] ~ N(0, (lora_b_gain^2) / r). With v ~ N(0, 1) entries, A v has unit-variance
+        entries and the delta B (A v) has standard deviation lora_b_gain (0.25) next to the base
+        product's ~1."""
+        s = self.shape
+        r, li = s.lora_rank, s.expert_in
+        assert r > 0
+        shapes = {"a_gate": (r, li), "b_gate": (s.h, r), "a_up": (r, li), "b_up": (s.h, r),
+                  "a_down": (r, s.h), "b_down": (li, r)}
+        stds = {"a_gate": li ** -0.5, "a_up": li ** -0.5, "a_down": s.h ** -0.5,
+                "b_gate": self.lora_b_gain * r ** -0.5, "b_up": self.lora_b_gain * r ** -0.5,
+                "b_down": self.lora_b_gain * r ** -0.5}
+        ids = dict(zip(LORA_NAMES, (LORA_A_GATE, LORA_B_GATE, LORA_A_UP, LORA_B_UP, LORA_A_DOWN, LORA_B_DOWN)))
+        c = 1 if count is None else count
+        out = {n: np.stack([bf16_normal(self.seed, ids[n], e, shapes[n], stds[n]) for e in range(e0, e0 + c)])
+               for n in LORA_NAMES}
+        if count is None:
+            out = {n: v[0] for n, v in out.items()}
+        return out
 
     def shared(self, j: int):
         s = self.shape
@@ -231,6 +257,21 @@ WORKLOADS = {
                                note="tiny conventional full-width MoE"),
     "tiny_skewed": Workload("tiny_skewed", LayerShape(d=256, l=128, h=96, E=16, k=4, Ns=2, hs=64), T=96,
                             seed=6, bias="zipf", zipf_alpha=0.3, note="tiny layer, Zipf-skewed bias, two shared"),
+    "tiny_lora": Workload("tiny_lora", LayerShape(d=256, l=128, h=96, E=16, k=4, Ns=1, hs=96, lora_rank=16), T=64,
+                          seed=12, note="tiny layer, rank-16 BF16 LoRA deltas on every routed expert matrix (panel "
+                                        "kernels)"),
+    "tiny_lora_mxfp8_many": Workload("tiny_lora_mxfp8_many", LayerShape(d=256, l=256, h=128, E=16, k=4, Ns=1, hs=96,
+                                                                        act="mxfp8", lora_rank=8), T=512, seed=13,
+                                     note="tiny layer, MXFP8, rank-8 LoRA, 128 rows per expert (scaled-MFMA "
+                                          "row-tiled kernels)"),
+    "tiny_lora_bf16_many": Workload("tiny_lora_bf16_many", LayerShape(d=256, l=128, h=128, E=16, k=4, Ns=1, hs=96,
+                                                                      lora_rank=32), T=512, seed=14,
+                                    note="tiny layer, bf16, rank-32 LoRA, 128 rows per expert (bf16 row-tiled "
+                                         "kernels)"),
+    "tiny_lora_split": Workload("tiny_lora_split", LayerShape(d=256, l=128, h=128, E=16, k=2, Ns=1, hs=96,
+                                                              lora_rank=16), T=128, seed=9, bias="zipf",
+                                zipf_alpha=0.3,
+                                note="as tiny_split with rank-16 LoRA: panel and row-tiled kernels in one stage"),
     "k3_decode_t64": Workload("k3_decode_t64", LayerShape(**K3), T=64, seed=1,
                               note="K3 shape decode, uniform routing (b = 0)"),
     "k3_decode_t512_zipf": Workload("k3_decode_t512_zipf", LayerShape(**K3), T=512, seed=1, bias="zipf",
@@ -241,6 +282,9 @@ WORKLOADS = {
                                         note="K3 shape decode, Zipf bias scaled to a 2-10x hot-expert load"),
     "k3_prefill_t8192": Workload("k3_prefill_t8192", LayerShape(**K3, act="mxfp8"), T=8192, seed=3,
                                  note="K3 shape prefill chunk, MXFP8 latent and hidden activations"),
+    "k3_decode_t64_lora": Workload("k3_decode_t64_lora", LayerShape(**K3, lora_rank=16), T=64, seed=1,
+                                   note="K3 shape decode (the T = 64 batch and weights of k3_decode_t64) with "
+                                        "rank-16 BF16 LoRA deltas on every routed expert matrix"),
     "k3_t2048": Workload("k3_t2048", LayerShape(**K3), T=2048, seed=3,
                          note="K3 shape, 2048 tokens, bf16 activations (the LatentMoE side of the "
                               "full-width T = 2048 comparison)"),

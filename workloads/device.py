@@ -20,10 +20,17 @@ from latent_width_expert_amd import K3MoE, LayerConfig
 from . import Workload
 
 
-def layer_config(shape, max_tokens: int) -> LayerConfig:
+def layer_config(shape, max_tokens: int, n_experts: int | None = None) -> LayerConfig:
     return LayerConfig(d_model=shape.d, latent=shape.l if shape.latent_moe else shape.d, hidden=shape.h,
-                       n_experts=shape.E, top_k=shape.k, n_shared=shape.Ns, shared_hidden=shape.hs,
-                       latent_moe=shape.latent_moe, act=shape.act, max_tokens=max_tokens, rms_eps=shape.eps)
+                       n_experts=shape.E if n_experts is None else n_experts, top_k=shape.k, n_shared=shape.Ns,
+                       shared_hidden=shape.hs, latent_moe=shape.latent_moe, act=shape.act, max_tokens=max_tokens,
+                       rms_eps=shape.eps, lora_rank=shape.lora_rank)
+
+
+def _lora_dev(stack, i, device):
+    """One expert's LoRA factors (bf16 bit patterns) as bf16 device tensors."""
+    return {n: torch.from_numpy(np.ascontiguousarray(v[i]).view(np.int16)).to(device).view(torch.bfloat16)
+            for n, v in stack.items()}
 
 
 def _dev(a, device):
@@ -54,28 +61,39 @@ def _log(msg):
     print(msg, file=sys.__stderr__, flush=True)
 
 
-def build_layer(provider, shape, max_tokens: int, device="cuda", chunk: int = 32, verbose: bool = False) -> K3MoE:
+def build_layer(provider, shape, max_tokens: int, device="cuda", chunk: int = 32, verbose: bool = False,
+                experts=None, dense: bool = True) -> K3MoE:
     """Create, allocate and pack a layer from a weight provider (a workloads.Workload or any
-    object with the same accessors). Returns the packed K3MoE."""
-    moe = K3MoE(layer_config(shape, max_tokens)).allocate(device)
+    object with the same accessors). Returns the packed K3MoE. experts: optional range of the
+    provider's routed experts to hold (one expert-parallel rank's share; the context then has
+    len(experts) experts); dense=False leaves the dense part unpacked (an expert-only rank)."""
+    ex = range(shape.E) if experts is None else experts
+    moe = K3MoE(layer_config(shape, max_tokens, n_experts=len(ex))).allocate(device)
     stream = torch.cuda.current_stream()
-    dense = upload_dense(provider, shape, device)
-    moe.pack(dense=dense)
-    stream.synchronize()
-    del dense
-    E = shape.E
-    many = isinstance(provider, Workload)
+    if dense:
+        dn = upload_dense(provider, shape, device)
+        moe.pack(dense=dn)
+        stream.synchronize()
+        del dn
+    E = len(ex)
+    base = ex.start
+    many = isinstance(provider, Workload) or getattr(provider, "chunked", False)
+    lora = shape.lora_rank > 0
 
     def produce(q):
         for e0 in range(0, E, chunk):
             n = min(chunk, E - e0)
+            g0 = base + e0
             if many:
-                q.put((e0, provider.routed(e0, n)))
+                mats = provider.routed(g0, n)
+                lo = provider.lora(g0, n) if lora else None
             else:
-                mats = [provider.routed(e) for e in range(e0, e0 + n)]
-                stack = tuple((np.stack([_one(m[i])[0] for m in mats]), np.stack([_one(m[i])[1] for m in mats]))
-                              for i in range(3))
-                q.put((e0, stack))
+                ms = [provider.routed(e) for e in range(g0, g0 + n)]
+                mats = tuple((np.stack([_one(m[i])[0] for m in ms]), np.stack([_one(m[i])[1] for m in ms]))
+                             for i in range(3))
+                los = [provider.lora(e) for e in range(g0, g0 + n)] if lora else None
+                lo = {k: np.stack([m[k] for m in los]) for k in los[0]} if lora else None
+            q.put((e0, mats, lo))
         q.put(None)
 
     q = queue.Queue(maxsize=2)
@@ -86,13 +104,14 @@ def build_layer(provider, shape, max_tokens: int, device="cuda", chunk: int = 32
         item = q.get()
         if item is None:
             break
-        e0, (g, u, d) = item
+        e0, (g, u, d), lo = item
         n = g[0].shape[0]
         gd, ud, dd = _pair(g, device), _pair(u, device), _pair(d, device)
         routed = [((gd[0][i], gd[1][i]), (ud[0][i], ud[1][i]), (dd[0][i], dd[1][i])) for i in range(n)]
-        moe.pack(routed=routed, routed_first=e0)
+        lod = [_lora_dev(lo, i, device) for i in range(n)] if lo is not None else None
+        moe.pack(routed=routed, routed_first=e0, lora=lod)
         stream.synchronize()
-        del gd, ud, dd, routed
+        del gd, ud, dd, routed, lod
         if verbose and (e0 // chunk) % 8 == 0:
             _log(f"[pack] experts {e0 + n}/{E} ({time.time() - t0:.1f} s)")
     th.join()
