@@ -206,6 +206,19 @@ int k3moe_forward_ex(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, 
                      void* stream, const k3moe_taps* taps);
 
 /*
+ * k3moe_forward for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the workspace is the library's static device
+ * scratch array (K3MOE_SCRATCH_BYTES per GPU, held until the process ends), so only x and y are
+ * passed. T's workspace must fit it (else K3MOE_ETOOBIG; at the K3 shape, decode batches up to 64
+ * tokens do); k3moe_scratch_fits tells. Calls on one GPU share that array: calls that overlap on
+ * one GPU (two streams, two threads) race. Nothing in the array needs clearing between calls.
+ */
+#define K3MOE_SCRATCH_BYTES ((size_t)64 << 20)
+int k3moe_forward_noalloc(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, void* stream);
+/* 1 when a forward of T tokens fits the static scratch, else 0. */
+int k3moe_scratch_fits(const k3moe_ctx* ctx, int32_t T);
+
+/*
  * Expert-parallel split of a forward ("Serving K3, 01 architecture": expert parallelism is mandatory
  * at scale and its all-to-all has data-dependent sizes; "Kimi K3: architectural innovations",
  * "Compress the expert interface": the latent z is what crosses the interconnect). With the experts in

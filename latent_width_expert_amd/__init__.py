@@ -105,6 +105,10 @@ def lib():
         L.k3moe_experts_forward.restype = ctypes.c_int
         L.k3moe_forward_tail.argtypes = [_vp, _vp, _i32, _vp, _vp, _vp]
         L.k3moe_forward_tail.restype = ctypes.c_int
+        L.k3moe_forward_noalloc.argtypes = [_vp, _vp, _i32, _vp, _vp]
+        L.k3moe_forward_noalloc.restype = ctypes.c_int
+        L.k3moe_scratch_fits.argtypes = [_vp, _i32]
+        L.k3moe_scratch_fits.restype = ctypes.c_int
         L.k3moe_stream_read.argtypes = [_vp, ctypes.c_size_t, _vp, _vp]
         L.k3moe_stream_read.restype = ctypes.c_int
         _lib = L
@@ -298,6 +302,18 @@ class K3MoE:
         bias = torch.empty(scores.shape[1], dtype=torch.float32, device=scores.device)
         self._check(self._L.k3moe_quantile_bias(self._h, _ptr(scores), scores.shape[0], _ptr(bias), _stream(stream)))
         return bias
+
+    # ---- no device allocation: the library's static scratch replaces the workspace
+    def scratch_fits(self, T: int) -> bool:
+        return bool(self._L.k3moe_scratch_fits(self._h, T))
+
+    def forward_noalloc(self, x, y, stream=None):
+        """k3moe_forward_noalloc: y (preallocated bf16 [T, d]) = layer(x), no workspace."""
+        T = x.shape[0]
+        _check_tensor("x", x, (T, self.cfg.d_model), (torch.bfloat16,))
+        _check_tensor("y", y, (T, self.cfg.d_model), (torch.bfloat16,))
+        self._check(self._L.k3moe_forward_noalloc(self._h, _ptr(x), T, _ptr(y), _stream(stream)))
+        return y
 
     # ---- expert-parallel split: head (origin) -> experts (each rank) -> tail (origin)
     def forward_head(self, x, n_ranks, stream=None):

@@ -846,6 +846,24 @@ int k3moe_forward(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, voi
   return k3moe_forward_ex(ctx, x_dev, T, y_dev, workspace_dev, stream, nullptr);
 }
 
+int k3moe_scratch_fits(const k3moe_ctx* ctx, int32_t T) {
+  if (!ctx || T < 0 || T > ctx->cfg.max_tokens) return 0;
+  return ws_layout(*ctx, T).total <= kScratchBytes ? 1 : 0;
+}
+
+int k3moe_forward_noalloc(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* y_dev, void* stream) {
+  if (!ctx) return K3MOE_EINVAL;
+  CHECK_OK(check_forward_args(ctx, x_dev, T, y_dev));
+  if (T == 0) return K3MOE_OK;
+  const WsLayout L = ws_layout(*ctx, T);
+  if (L.total > kScratchBytes)
+    return fail(ctx, K3MOE_ETOOBIG, "T = %d needs %zu bytes of workspace, above the %zu-byte static scratch", T,
+                L.total, kScratchBytes);
+  void* scratch_ptr = nullptr;  // this device's copy of the static scratch array
+  HIPCHECK(ctx, scratch_address(&scratch_ptr), "scratch address");
+  return forward_impl(ctx, x_dev, T, y_dev, (uint8_t*)scratch_ptr, L, (hipStream_t)stream, nullptr);
+}
+
 int k3moe_forward_head(k3moe_ctx* ctx, const void* x_dev, int32_t T, void* workspace_dev, void* stream,
                        int32_t n_ranks, void* send_rows_dev, uint8_t* send_scales_dev, int32_t* send_counts_dev,
                        int32_t* expert_counts_dev) {

@@ -181,6 +181,11 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t s);
 // Streaming read of `bytes` (a multiple of 16) with non-temporal 16-byte loads; the xor of every word
 // read is xor-ed into *out (a measurement of the plain HBM read rate).
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s);
+
+// The library's static device scratch (for callers that cannot allocate): its address on the current
+// device (looked up once per device) and its size.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+hipError_t scratch_address(void** out);
 // b_e = -(m-th largest of scores[:, e]) for T <= 16384 calibration tokens ([T, E] fp32 scores)
 hipError_t launch_quantile_bias(const float* scores, int T, int E, int m, float* bias, hipStream_t s);
 

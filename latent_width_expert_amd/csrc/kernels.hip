@@ -8,6 +8,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -2237,6 +2238,37 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hip
   const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(n16, 256 * 4), 256 * 16);
   hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, s, buf, n16, out);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Static device scratch for the entry point that allocates nothing. Each GPU the library runs on holds
+// its own copy of the array (allocated when the code object is loaded there) until the process ends.
+// Host code never uses the array's name as a device address: its address on each device is looked up
+// once, with that device current, and kept.
+// ---------------------------------------------------------------------------------------------
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace k3

@@ -128,6 +128,9 @@ def test_new_entry_points_check_arguments_before_any_device_work():
     assert L.k3moe_experts_forward(m._h, None, None, 8, None, None, None, None) == k3.ESTATE
     assert L.k3moe_forward_tail(m._h, None, 4, None, None, None) == k3.ESTATE
     assert L.k3moe_forward_tail(m._h, None, 65, None, None, None) == k3.ETOOBIG
+    # no-allocation forward: same checks as forward
+    assert L.k3moe_forward_noalloc(m._h, None, 4, None, None) == k3.ESTATE
+    assert L.k3moe_forward_noalloc(m._h, None, 65, None, None) == k3.ETOOBIG
     # LoRA factors are required when the rank is set
     w = k3.Weights()
     w.routed_first, w.routed_count = 0, 1
@@ -144,3 +147,11 @@ def test_new_entry_points_check_arguments_before_any_device_work():
 def test_create_rejects_bad_lora_rank(rank):
     with pytest.raises(k3.K3MoEError):
         k3.K3MoE(_cfg(lora_rank=rank))
+
+
+def test_scratch_fits():
+    """The static scratch holds a K3-shape decode batch of 64 tokens, not a prefill chunk."""
+    m = k3.K3MoE(LayerConfig(d_model=7168, latent=3584, hidden=3072, n_experts=896, top_k=16, n_shared=2,
+                             shared_hidden=3072, max_tokens=8192))
+    assert m.scratch_fits(64) and not m.scratch_fits(8192)
+    assert not m.scratch_fits(8193) and not m.scratch_fits(-1)

@@ -224,7 +224,7 @@ def test_k3_prefill_t8192_mxfp8():
     c = g["counts"]
     hot = int(np.argmax(c))
     ragged = [int(e) for e in np.nonzero(c % 192 != 0)[0] if e >= 512][:4]
-    experts = sorted(set(np.linspace(0, 895, 56).round().astype(int).tolist()) | {hot} | set(ragged) |
+    experts = sorted(set(np.linspace(0, 895, 64).round().astype(int).tolist()) | {hot} | set(ragged) |
                      set(range(512, 516)))
     assert len(experts) >= 64
     wh, wo, rows = stagewise_experts(wl, g, experts)
