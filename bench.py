@@ -175,13 +175,13 @@ def counts_of(moe, x, y, E):
 
 
 def stream_read_gbps(dev):
-    """Plain streaming read of 4 GiB (k3moe_stream_read), median of 5."""
+    """Plain streaming read of 4 GiB (k3moe_stream_read): 2 warm-up calls, then 5 back to back."""
     import torch
     import latent_width_expert_amd as lwe
     buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
     buf.fill_(1)
     chk = torch.zeros(1, dtype=torch.int32, device=dev)
-    ms = sorted(time_call(lambda: lwe.stream_read(buf, chk), 1, 1 if i == 0 else 0) for i in range(5))[2]
+    ms = time_call(lambda: lwe.stream_read(buf, chk), 5, 2)
     del buf, chk
     return (4 << 30) / (ms * 1e-3) / 1e9
 

@@ -101,6 +101,7 @@ struct GemmArgs {
                            // the others the panel kernel (both launched; each skips the other's groups)
   int32_t row_cap;         // grouped, row-tiled kernel: when > 0, groups of row_cap or more rows are left to
                            // another row-tiled launch (set by the launcher)
+  int32_t panel_major;     // dense, row-tiled kernel: blocks dealt panel block first (set by the launcher)
   int32_t* items;          // grouped, row-tiled kernel: workspace of tile_items_bytes() for the work-item
                            // list (persistent grid); null: one block per (group, panel block)
   int32_t nseg;

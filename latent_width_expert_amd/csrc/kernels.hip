@@ -726,6 +726,15 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
     it = args.items[xcd] + slot;
     it_end = args.items[xcd + 1];
     it_step = (int)gridDim.x / 8;
+  } else if (DENSE && args.panel_major) {
+    // few row chunks: panel block p on XCD p mod 8 with every chunk of it side by side there, so each
+    // weight panel is streamed from HBM once and the chunks re-read it from that L2 (the activation
+    // rows, a few MB, are what every XCD reads)
+    cpanel0 = 4 * (xcd + 8 * (slot / ngrp));
+    cgrp = slot % ngrp;
+    if (cpanel0 >= args.P) return;
+    cmb = cgrp * ROWS;
+    cr1 = min(cmb + ROWS, args.M);
   } else {
     const bool spread = ngrp < 8;
     cgrp = spread ? (int)blockIdx.x / nblk : xcd + 8 * (slot / nblk);
@@ -1081,6 +1090,328 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
   }
 }
 
+
+// Row-tiled grouped GEMM for MXFP8 activations (prefill gate/up and down): MXFP4 weights against
+// E4M3 activation rows on the scaled MFMA, with the weights kept out of LDS.
+// Block: 8 waves (2 per SIMD) on one expert's chunk of up to 192 rows and 4 consecutive panels; wave
+// (pg, h) computes panel panel0 + pg on row tiles h, h + 2, ... (6 row tiles x 4 column tiles of 16).
+// Per 128-K window:
+//   - the wave's own panel-window is loaded straight into a register ring DB windows ahead with the
+//     non-temporal policy (the weights stream from HBM once): each lane's 16 bytes are already its MFMA
+//     operand, so the weights never pass through LDS;
+//   - the chunk's activation rows (E4M3 codes and E8M0 scales, mostly L2 hits: the expert's other
+//     panel blocks read the same rows) are loaded into registers DA windows ahead, each wave 24 rows
+//     (three 16-byte pieces a lane; waves 0..2 also one scale word a lane), and written to one of two
+//     LDS stages the window before they are used (16-byte chunk c of row r at position c ^ (r & 7), so
+//     the operand reads are conflict-free); all eight waves read the operands of their tiles from it.
+// Every load is compiler-visible, so the compiler's waits cover exactly the loads a use depends on;
+// one LDS wait and one barrier per window order the stages. Units (expert, chunk, panel block) come
+// from the XCD's work-item list as in tiled_gemm_kernel; the next unit's first loads are issued before
+// the current unit's epilogue.
+// EPI 0: fp32 out. EPI 1: GLU panels, SiLU(gate) * up MX-encoded (E4M3, E8M0 per 32 units), staged in
+// LDS and written as 16-byte row segments.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only: this wave's LDS writes and reads are done
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int NWAVE, int DA, int DB, int EPI, int TAG>
+__global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(NWAVE / 4, NWAVE / 4)))
+void tiled_f8_kernel(GemmArgs args) {
+  constexpr int MT = 12, ROWS = 16 * MT, NPG = 4, NPH = NWAVE / NPG, MTW = MT / NPH;
+  constexpr int AROW = 128, A_SC = ROWS * AROW, A_STAGE = A_SC + ROWS * 4;
+  constexpr int NB = DB + 1;
+  constexpr int APL = ROWS * AROW / (16 * 64 * NWAVE);  // 16-byte activation pieces per lane and window
+  constexpr int SCW = ROWS / 64;                         // waves that load a scale word per lane
+  constexpr int U = NB % 2 == 0 ? NB : 2 * NB;           // windows per unrolled step (stage, set, slot cycle)
+  static_assert(APL * 16 * 64 * NWAVE == ROWS * AROW && ROWS % 64 == 0 && U % DA == 0 && (DA == 1 || DA == 2),
+                "shape");
+  static_assert(ROWS * 132 <= A_STAGE, "epilogue staging fits one stage");
+  static_assert(EPI == 0 || EPI == 1, "epilogue");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][A_STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pg = wv % NPG, h = wv / NPG;
+  const int g = lane >> 4, i16 = lane & 15;
+  const rsrc_t ar = make_rsrc(args.A, args.a_bytes);
+  const rsrc_t asr = make_rsrc(args.A_scales, args.as_bytes);
+  const int nwin = args.wwin;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const bool listed = args.items != nullptr;
+  const int nblk = (args.P + 3) / 4;
+  int it = 0, it_end = 0, it_step = 1;
+  int cgrp = 0, cpanel0 = 0, cmb = 0, cr1 = 0;
+  if (listed) {
+    it = args.items[xcd] + slot;
+    it_end = args.items[xcd + 1];
+    it_step = (int)gridDim.x / 8;
+  } else {
+    const bool spread = args.n_groups < 8;
+    cgrp = spread ? (int)blockIdx.x / nblk : xcd + 8 * (slot / nblk);
+    cpanel0 = 4 * (spread ? (int)blockIdx.x % nblk : slot % nblk);
+    if (cgrp >= args.n_groups) return;
+    cmb = args.offsets[cgrp];
+    cr1 = args.offsets[cgrp + 1];
+    if (cmb >= cr1) return;
+    if (cr1 - cmb < args.row_split || (args.row_cap > 0 && cr1 - cmb >= args.row_cap)) return;
+  }
+  // the unit in hand and the per-lane sources of its loads
+  int grp = 0, panel0 = 0, mb = 0, r1 = 0, npan = 0;
+  rsrc_t wr = make_rsrc(nullptr, 0);
+  int aoff[APL], soff = -1;
+  auto next_unit = [&]() __attribute__((always_inline)) -> bool {
+    if (listed) {
+      if (it >= it_end) return false;
+      const u32 item = (u32)args.items[kItemHeader + it];
+      it += it_step;
+      grp = (int)(item & 0xFFFu);
+      panel0 = 4 * (int)(item >> 24);
+      mb = args.offsets[grp] + ROWS * (int)((item >> 12) & 0xFFFu);
+      r1 = min(mb + ROWS, args.offsets[grp + 1]);
+    } else {
+      if (cmb >= cr1) return false;
+      grp = cgrp;
+      panel0 = cpanel0;
+      mb = cmb;
+      r1 = cr1;
+      cmb += ROWS;
+    }
+    grp = __builtin_amdgcn_readfirstlane(grp);
+    panel0 = __builtin_amdgcn_readfirstlane(panel0);
+    mb = __builtin_amdgcn_readfirstlane(mb);
+    r1 = __builtin_amdgcn_readfirstlane(r1);
+    npan = min(4, args.P - panel0);
+    // this wave's panel (zeros when the panel block is short)
+    wr = make_rsrc(args.W + (int64_t)grp * args.w_group_stride + (int64_t)(panel0 + pg) * nwin * kPanelWinBytes,
+                   pg < npan ? (int64_t)nwin * kPanelWinBytes : 0);
+    // activation piece j of this lane: chunk row 24 wv + 8 j + lane / 8, LDS position lane % 8 holding the
+    // row's 16-byte chunk (lane % 8) ^ (row & 7); rows past the chunk read zeros
+#pragma unroll
+    for (int j = 0; j < APL; ++j) {
+      const int r = (ROWS / NWAVE) * wv + 8 * j + lane / 8;
+      const int c = (lane % 8) ^ (r & 7);
+      aoff[j] = mb + r < r1 ? (args.rowmap ? args.rowmap[mb + r] : mb + r) * (int)args.lda + 16 * c : -1;
+    }
+    if (wv < SCW) {
+      const int r = 64 * wv + lane;
+      soff = mb + r < r1 ? (args.rowmap ? args.rowmap[mb + r] : mb + r) * (int)args.ldas : -1;
+    }
+    return true;
+  };
+
+  struct AWinR {  // one window's activation pieces of this lane
+    u32x4 c[APL];
+    u32 sc;
+  };
+  struct BWinR {  // one window of this wave's panel
+    u32x4 c[4];
+    u32 sc;
+  };
+  AWinR ast[DA];
+  BWinR bring[NB];
+  // The window index passes through an empty asm statement: the offsets are then formed where the loads
+  // are issued instead of being precomputed for every unrolled window (which would hold them in VGPRs).
+  auto load_a = [&](AWinR& a, int w) __attribute__((always_inline)) {
+    asm volatile("" : "+s"(w));
+    const bool in = w < nwin;
+#pragma unroll
+    for (int j = 0; j < APL; ++j)
+      a.c[j] = __builtin_amdgcn_raw_buffer_load_b128(ar, in && aoff[j] >= 0 ? aoff[j] + AROW * w : kOOB, 0, 0);
+    if (wv < SCW) a.sc = __builtin_amdgcn_raw_buffer_load_b32(asr, in && soff >= 0 ? soff + 4 * w : kOOB, 0, 0);
+  };
+  auto store_a = [&](const AWinR& a, int stage) __attribute__((always_inline)) {
+    uint8_t* base = &lds_a[stage][0];
+#pragma unroll
+    for (int j = 0; j < APL; ++j) *(u32x4*)(base + 1024 * (APL * wv + j) + 16 * lane) = a.c[j];
+    if (wv < SCW) *(u32*)(base + A_SC + 256 * wv + 4 * lane) = a.sc;
+  };
+  auto load_b = [&](BWinR& b, int w) __attribute__((always_inline)) {
+    asm volatile("" : "+s"(w));
+    const int off = w < nwin ? w * kPanelWinBytes : kOOB;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) b.c[rt] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + rt * 1024 + lane * 16, 0, kNT);
+    b.sc = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 4096 + lane * 4, 0, kNT);
+  };
+  // first loads of a unit: A(0), A(1) into the staging sets, B(0 .. DB - 1) into the ring
+  auto prologue_loads = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < DA; ++n) load_a(ast[n], n);
+#pragma unroll
+    for (int n = 0; n < DB; ++n) load_b(bring[n], n);
+  };
+  // A(0) to stage 0, then A(DA) into the set it came from (one set: A(1) once A(0) is written)
+  auto prologue_store = [&]() __attribute__((always_inline)) {
+    store_a(ast[0], 0);
+    load_a(ast[0], DA);
+  };
+
+  f32x4 acc[MTW][4];
+  bool have = next_unit();
+  if (have) {
+    prologue_loads();
+    prologue_store();
+  }
+  while (have) {
+    const int nt = min(MT, (r1 - mb + 15) / 16);
+    const int nw = nt > h ? (nt - h + NPH - 1) / NPH : 0;  // this wave's row tiles holding rows
+#pragma unroll
+    for (int j = 0; j < MTW; ++j)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[j][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto run = [&]<int N>() __attribute__((always_inline)) {
+      for (int w0 = 0; w0 < nwin; w0 += U) {
+        [&]<int... UI>(std::integer_sequence<int, UI...>) __attribute__((always_inline)) {
+          ([&]() __attribute__((always_inline)) {
+            constexpr int u = UI;
+            const int w = w0 + u;
+            if (w < nwin) {  // uniform
+              lds_barrier();  // A(w) in its stage for every wave; every wave done with window w - 1
+              if (w + 1 < nwin) store_a(ast[(u + 1) % DA], (u + 1) & 1);
+              load_a(ast[(u + 1) % DA], w + 1 + DA);
+              load_b(bring[(u + DB) % NB], w + DB);
+              if constexpr (N > 0) {
+                const BWinR& bw = bring[u % NB];
+                const uint8_t* sa = lds_a[u & 1];
+                const uint8_t* prow = sa + i16 * AROW + h * 16 * AROW;
+                const uint8_t* psc = sa + A_SC + i16 * 4 + g + h * 64;
+                auto tile = [&](int j, i32x8& op, int& sc) __attribute__((always_inline)) {
+                  const uint8_t* pr = prow + j * NPH * 16 * AROW;
+                  const u32x4 lo = *(const u32x4*)(pr + 16 * (g ^ (i16 & 7)));
+                  const u32x4 hi = *(const u32x4*)(pr + 16 * ((4 + g) ^ (i16 & 7)));
+                  sc = psc[j * NPH * 64];
+                  op = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+                };
+                i32x8 cur;
+                int csc;
+                tile(0, cur, csc);
+                [&]<int... JI>(std::integer_sequence<int, JI...>) __attribute__((always_inline)) {
+                  ([&]() __attribute__((always_inline)) {
+                    constexpr int j = JI;
+                    i32x8 nxt;
+                    int nsc = 0;
+                    if constexpr (j + 1 < N) tile(j + 1, nxt, nsc);
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct) {
+                      const i32x8 bop = {(int)bw.c[ct][0], (int)bw.c[ct][1], (int)bw.c[ct][2], (int)bw.c[ct][3], 0, 0, 0, 0};
+                      acc[j][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur, bop, acc[j][ct], 0, 4, 0, csc, 0,
+                                                                                    (int)(bw.sc >> (8 * ct)));
+                    }
+                    if constexpr (j + 1 < N) {
+                      cur = nxt;
+                      csc = nsc;
+                    }
+                  }(), ...);
+                }(std::make_integer_sequence<int, N>{});
+              }
+            }
+          }(), ...);
+        }(std::make_integer_sequence<int, U>{});
+      }
+    };
+    [&]<int... I>(std::integer_sequence<int, I...>) __attribute__((always_inline)) {
+      ((nw == I ? (run.template operator()<I>(), 0) : 0), ...);
+    }(std::make_integer_sequence<int, MTW + 1>{});
+
+    // Every wave done with the stages; the next unit's first loads go out before this unit's epilogue
+    // (which stages in LDS) and its first LDS write after it.
+    lds_barrier();
+    const int e_mb = mb, e_r1 = r1, e_panel0 = panel0, e_npan = npan, e_grp = grp;
+    have = next_unit();
+    // the GLU epilogue's arithmetic covers the next unit's first loads; the fp32 one is only stores
+    if (EPI == 1 && have) prologue_loads();
+    {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));  // lane indices re-derived so no address arithmetic is hoisted
+      const int eg = ln >> 4, ej = ln & 15;
+      const EpiSeg& sg = args.seg[0];
+      const int nrow = min(ROWS, e_r1 - e_mb);
+      // LoRA deltas (the row-tiled launches need whole 64-column panels, so every column of a panel
+      // below npan is a real one)
+      if (args.lora_t) {
+#pragma unroll
+        for (int j = 0; j < MTW; ++j) {
+          const int row0 = e_mb + 16 * (h + NPH * j) + 4 * eg;
+          if (pg < e_npan && row0 < e_r1) {
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+              const int col = EPI == 1 ? 32 * (e_panel0 + pg) + 16 * (ct >> 1) + ej : 64 * (e_panel0 + pg) + 16 * ct + ej;
+              const int q0 = EPI == 1 && (ct & 1) ? args.lora_rank : 0;
+              lora_add(args, acc[j][ct], e_grp, row0, e_r1, col, q0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (EPI == 1) {
+        // codes staged as [ROWS][128 bytes] (32 units per panel), scales as [ROWS][4]
+        uint8_t* stg = &lds_a[0][0];
+        uint8_t* stg_sc = stg + ROWS * 128;
+        const bool tap = sg.pre != nullptr;
+        const rsrc_t prr = make_rsrc(tap ? sg.pre + (int64_t)e_mb * sg.ldpre : nullptr, tap ? (int64_t)nrow * sg.ldpre * 4 : 0);
+#pragma unroll
+        for (int j = 0; j < MTW; ++j) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float v0 = silu(acc[j][0][r]) * acc[j][1][r];
+            const float v1 = silu(acc[j][2][r]) * acc[j][3][r];
+            const int lr = 16 * (h + NPH * j) + 4 * eg + r;
+            if (tap) {
+              const int o = lr * (int)sg.ldpre + sg.col0 + 32 * (e_panel0 + pg) + ej;
+              const bool ok = lr < nrow && pg < e_npan;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), prr, ok ? 4 * o : kOOB, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), prr, ok ? 4 * (o + 16) : kOOB, 0, 0);
+            }
+            u32 c0, c1, sb;
+            mxfp8_block(v0, v1, c0, c1, sb);
+            stg[lr * 128 + 32 * pg + ej] = (uint8_t)c0;
+            stg[lr * 128 + 32 * pg + 16 + ej] = (uint8_t)c1;
+            stg_sc[lr * 4 + pg] = (uint8_t)sb;  // the 16 lanes of the block agree
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        lds_barrier();
+        const int t = threadIdx.x;
+        uint8_t* out = (uint8_t*)sg.out + sg.col0 + 32 * e_panel0;
+#pragma unroll
+        for (int q = 0; q < ROWS / (8 * NWAVE); ++q) {
+          const int lr = 8 * NWAVE * q + t / 8, piece = t % 8;
+          if (lr < nrow && piece < 2 * e_npan)
+            *(u32x4*)(out + (int64_t)(e_mb + lr) * sg.ldo + 16 * piece) = *(const u32x4*)(stg + lr * 128 + 16 * piece);
+        }
+        for (int lr = t; lr < nrow; lr += 64 * NWAVE) {
+          uint8_t* os = sg.out_scales + (int64_t)(e_mb + lr) * sg.ldos + sg.col0 / 32 + e_panel0;
+          if (e_npan == 4)
+            *(u32*)os = *(const u32*)(stg_sc + 4 * lr);
+          else
+            for (int p = 0; p < e_npan; ++p) os[p] = stg_sc[4 * lr + p];
+        }
+        lds_barrier();  // staging read by every wave before the next unit's first LDS write
+      } else {
+        const rsrc_t orr = make_rsrc((float*)sg.out + (int64_t)e_mb * sg.ldo + sg.col0, (int64_t)nrow * sg.ldo * 4);
+        const int ldo = (int)sg.ldo;
+#pragma unroll
+        for (int j = 0; j < MTW; ++j) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int lr = 16 * (h + NPH * j) + 4 * eg + r;
+            const int base = 4 * (lr * ldo + 64 * (e_panel0 + pg) + ej);
+            const bool rok = lr < nrow && pg < e_npan;
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+              const bool ok = rok && 64 * (e_panel0 + pg) + 16 * ct + ej < sg.ncols;
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][ct][r]), orr, ok ? base + 64 * ct : kOOB, 0, 0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    if (EPI == 0 && have) prologue_loads();
+    if (have) prologue_store();
+  }
+}
 
 // Skinny dense GEMM (at most 64 rows, e.g. a decode batch against x's or the output's weights).
 // With few rows the weights are the whole stream and the activation window (64 rows x 128 K) is
@@ -1441,8 +1772,21 @@ static void launch_grouped_tiled(const GemmArgs& a, hipStream_t s) {
 
 template <int EPI, int TAG>
 static void launch_f8(const GemmArgs& a, hipStream_t s) {
-  // 192-row chunks; activation rows 3 windows ahead, weights 2
-  launch_grouped_tiled<3, 2, 12, EPI, TAG, A_MXFP8>(a, s);
+  if constexpr (EPI == 0) {
+    // down (fp32 out): both operands through LDS-DMA; activation rows 3 windows ahead, weights 2
+    launch_grouped_tiled<3, 2, 12, EPI, TAG, A_MXFP8>(a, s);
+  } else {
+    // gate/up: 192-row chunks on 8 waves, weights 2 windows ahead in registers, activation rows 2 ahead
+    constexpr int NW = 8, DB = 2, DA = 2;
+    const unsigned nblk = (unsigned)ceil_div(a.P, 4);
+    unsigned grid = (unsigned)ceil_div(a.n_groups, 8) * 8 * nblk;
+    if (a.items) {
+      hipLaunchKernelGGL(tile_items_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.n_groups, a.row_split, a.row_cap,
+                         192, (int)nblk, a.items);
+      grid = kItemGrid;
+    }
+    hipLaunchKernelGGL((tiled_f8_kernel<NW, DA, DB, EPI, TAG>), dim3(grid), dim3(64 * NW), 0, s, a);
+  }
 }
 
 // bf16 grouped, the weights converted to bf16 operands once per window. Experts below 64 rows: 64-row
@@ -1478,9 +1822,12 @@ static void launch_dense_tiled(const GemmArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, true, 2, 2, kDenseRows / 16, WPS, PPW, 2, TAG>), dim3(g8 * nblk),
                        dim3(256 * WPS), 0, s, a);
   } else {
-    const unsigned g8 = (unsigned)ceil_div(ceil_div(a.M, 64), 8) * 8;
-    hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, true, 3, 4, 4, WPS, PPW, 2, TAG>), dim3(g8 * nblk), dim3(256 * WPS),
-                       0, s, a);
+    // 64-row chunks, panel-major: the grid covers every (panel block, chunk), XCD by XCD
+    GemmArgs b = a;
+    b.panel_major = 1;
+    const unsigned nch = (unsigned)ceil_div(a.M, 64);
+    hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, true, 3, 4, 4, WPS, PPW, 2, TAG>), dim3(ceil_div(nblk, 8) * 8 * nch),
+                       dim3(256 * WPS), 0, s, b);
   }
 }
 
@@ -2007,8 +2354,8 @@ hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, int64_t n, hipStre
 // matrix); the second factor is added in the grouped GEMMs' epilogues (lora_add).
 // One block of 4 waves per group: the group's rows in chunks of 64 (4 row tiles of 16); wave w takes
 // K windows w, w + 4, ... of 128; per window, lane (i, g) holds K [128 w + 32 g, +32) of row / column i
-// and four bf16 MFMA 16x16x32 steps cover it. The four waves' sums are added in wave order through
-// LDS (deterministic).
+// and four bf16 MFMA 16x16x32 steps cover it. The waves' sums are added in wave order through LDS
+// (deterministic).
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ void lora_act_load(const LoraAArgs& a, rsrc_t ar, rsrc_t asr, int arow, bool ok, int kb,
                                               bf16x8 (&v)[4]) {
@@ -2036,8 +2383,9 @@ __device__ __forceinline__ void lora_act_load(const LoraAArgs& a, rsrc_t ar, rsr
   }
 }
 
-__global__ __launch_bounds__(256) void lora_a_kernel(LoraAArgs a) {
-  __shared__ f32x4 red[3][4][4][64];
+constexpr int kLoraWaves = 4;
+__global__ __launch_bounds__(64 * kLoraWaves) void lora_a_kernel(LoraAArgs a) {
+  __shared__ f32x4 red[kLoraWaves][4][64];  // one row tile's partial sums of every wave
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = blockIdx.x;
@@ -2064,7 +2412,7 @@ __global__ __launch_bounds__(256) void lora_a_kernel(LoraAArgs a) {
       aok[rt] = rt < nrt && row < r1;
       arow[rt] = aok[rt] ? (a.rowmap ? a.rowmap[row] : row) : 0;
     }
-    for (int w = wv; w < nwin; w += 4) {
+    for (int w = wv; w < nwin; w += kLoraWaves) {
       const int kb = 4 * w + g;
       bf16x8 bv[4][4];
 #pragma unroll
@@ -2087,38 +2435,35 @@ __global__ __launch_bounds__(256) void lora_a_kernel(LoraAArgs a) {
         }
       }
     }
-    if (wv > 0) {
+    // the waves' partial sums, one row tile at a time, added in wave order (deterministic)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < 4; ++rt) {
+      if (rt < nrt) {  // uniform
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) red[wv - 1][rt][ct][lane] = acc[rt][ct];
-    }
-    __syncthreads();
-    if (wv == 0) {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          f32x4 v = acc[rt][ct];
-#pragma unroll
-          for (int q = 0; q < 3; ++q) v += red[q][rt][ct][lane];
+        for (int ct = 0; ct < 4; ++ct) red[wv][ct][lane] = acc[rt][ct];
+        __syncthreads();
+        if (wv < nct) {  // wave ct adds column tile ct
+          const int ct = wv;
+          f32x4 v = red[0][ct][lane];
+          for (int q = 1; q < kLoraWaves; ++q) v += red[q][ct][lane];
           // D lane (j, g): column 16 ct + j, rows 16 rt + 4 g + r
           const int n = 16 * ct + i16;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int row = mb + 16 * rt + 4 * g + r;
-            if (rt < nrt && row < r1 && n < a.N) a.t[(int64_t)row * a.ldt + n] = v[r];
+            if (row < r1 && n < a.N) a.t[(int64_t)row * a.ldt + n] = v[r];
           }
         }
+        __syncthreads();
+      }
     }
-    __syncthreads();
   }
 }
 
 hipError_t launch_lora_a(const LoraAArgs& a, hipStream_t s) {
   if (a.n_groups <= 0) return hipSuccess;
   if (a.N < 8 || a.N > 64 || a.N % 8 || a.K % 32 || a.K <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(lora_a_kernel, dim3((unsigned)a.n_groups), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(lora_a_kernel, dim3((unsigned)a.n_groups), dim3(64 * kLoraWaves), 0, s, a);
   return hipGetLastError();
 }
 
@@ -2209,24 +2554,27 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t s) 
 }
 
 // ---------------------------------------------------------------------------------------------
-// Plain streaming read (measurement of the HBM read rate a simple kernel reaches): every 16 bytes
-// read once with non-temporal loads, four loads in flight per thread, the xor of all words folded
-// into one word (so that no load is dead).
+// Plain streaming read (measurement of the HBM read rate a simple kernel reaches): block b reads a
+// contiguous range of the buffer once, 256 threads x 16 bytes a load, eight non-temporal loads in
+// flight per thread (the way the weight streams of the grouped GEMMs load); the xor of every word is
+// folded into one word so that no load is dead.
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void stream_read_kernel(const void* buf, int64_t n16, uint32_t* out) {
-  const u32x4* p = (const u32x4*)buf;
-  const int64_t stride = (int64_t)gridDim.x * 256;
+constexpr int kStreamBlocks = 256 * 8;
+constexpr int kStreamUnroll = 8;
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint8_t* buf, int64_t per, int64_t bytes, uint32_t* out) {
+  const int64_t b0 = (int64_t)blockIdx.x * per;
+  const int64_t n = min(per, bytes - b0);
   u32 acc = 0;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = __builtin_nontemporal_load(p + i), b = __builtin_nontemporal_load(p + i + stride);
-    const u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride), d = __builtin_nontemporal_load(p + i + 3 * stride);
-    const u32x4 x = a ^ b ^ c ^ d;
-    acc ^= x[0] ^ x[1] ^ x[2] ^ x[3];
-  }
-  for (; i < n16; i += stride) {
-    const u32x4 a = __builtin_nontemporal_load(p + i);
-    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  if (n > 0) {
+    const rsrc_t r = make_rsrc(buf + b0, n);
+    const int t16 = threadIdx.x * 16;
+    for (int64_t o = 0; o < n; o += 4096 * kStreamUnroll) {
+      u32x4 v[kStreamUnroll];
+#pragma unroll
+      for (int i = 0; i < kStreamUnroll; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)o + t16 + 4096 * i, 0, kNT);
+#pragma unroll
+      for (int i = 0; i < kStreamUnroll; ++i) acc ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
+    }
   }
   for (int off = 32; off >= 1; off >>= 1) acc ^= (u32)__shfl_xor((int)acc, off);
   if ((threadIdx.x & 63) == 0) atomicXor(out, acc);
@@ -2234,9 +2582,10 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const void* buf, int64
 
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t s) {
   if (bytes <= 0 || bytes % 16 || !buf || !out) return hipErrorInvalidValue;
-  const int64_t n16 = bytes / 16;
-  const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(n16, 256 * 4), 256 * 16);
-  hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, s, buf, n16, out);
+  // equal contiguous ranges (multiples of 16 bytes, each below 2 GiB for the 32-bit buffer offsets)
+  const int64_t per = (ceil_div(ceil_div(bytes, kStreamBlocks), 16)) * 16;
+  if (per >= ((int64_t)1 << 31) - 4096 * kStreamUnroll) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(kStreamBlocks), dim3(256), 0, s, (const uint8_t*)buf, per, bytes, out);
   return hipGetLastError();
 }
 

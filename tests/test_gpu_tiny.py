@@ -218,9 +218,10 @@ def test_split_by_rows_ragged(name, T):
     check_all(name, T)
 
 
-@pytest.mark.parametrize("T", [1024, 1500])
+@pytest.mark.parametrize("T", [700, 1024, 1500])
 def test_dense_many_rows_ragged(T):
-    """Row-tiled dense GEMMs: 128-row chunks with a partial last chunk."""
+    """Row-tiled dense GEMMs with a partial last chunk: 64-row chunks dealt panel block first (T = 700),
+    128-row chunks dealt chunk first (T >= 1024)."""
     check_all("tiny_dense_many", T)
 
 
