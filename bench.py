@@ -325,6 +325,8 @@ def main():
                         "gateup": rf, "stages_ms": st, "expert_load": load_summary(c)}
             log(f"[bench] {name}: {ms:.4f} ms/step, {sk[name]['layer_hbm_gbps']:.0f} GB/s, "
                 f"max/mean {sk[name]['expert_load']['max_over_mean']:.2f}")
+            if name == "k3_decode_t512_zipf":
+                sk["quantile_balancing"] = quantile_balancing(moe, wz, xz, yz, c, sec_steps, stream_gbps)
         out["skewed"] = sk
         moe.pack(dense=wdev.upload_dense(wl, s))
         torch.cuda.synchronize()
@@ -465,6 +467,57 @@ def main():
         torch.cuda.synchronize()
         res["calib_copy_bytes"] = n
     print(json.dumps(res), flush=True)
+
+
+def rank_loads(counts, n_ranks=8):
+    """Rows each of n_ranks contiguous expert ranges receives: max over mean."""
+    import numpy as np
+    r = np.asarray(counts).reshape(n_ranks, -1).sum(axis=1)
+    return float(r.max() / max(r.mean(), 1e-9))
+
+
+def quantile_balancing(moe, wz, xz, yz, counts_before, steps, stream_gbps):
+    """Quantile Balancing at K3 shape on the literal-Zipf router: the bias from the router scores of a
+    held-out calibration batch (the next T tokens of the same stream) by k3moe_quantile_bias, packed
+    in place of the Zipf bias, then the bench batch run with it. Each expert's calibration cutoff
+    admits m = round(T k / E) tokens (s + b >= 0); the loads of the top-k selection are reported
+    against the mean T k / E, per expert and per contiguous range of E / 8 experts."""
+    import numpy as np
+    import torch
+    import workloads.device as wdev
+    s = wz.shape
+    cal = torch.from_numpy(wz.x_bits(2 * wz.T)[wz.T:].view(np.int16)).to(xz.device).view(torch.bfloat16)
+    scores = torch.empty(wz.T, s.E, dtype=torch.float32, device=xz.device)
+    moe.forward(cal, torch.empty_like(cal), taps={"scores": scores})
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    bias = moe.quantile_bias(scores)
+    ev1.record()
+    torch.cuda.synchronize()
+    cal_ms = ev0.elapsed_time(ev1)
+    # cutoff check on the calibration batch: tokens with s + b >= 0 per expert
+    admitted = ((scores + bias[None, :]) >= 0).sum(dim=0).cpu().numpy()
+    dense = wdev.upload_dense(wz, s)
+    dense["router_bias"] = bias
+    moe.pack(dense=dense)
+    torch.cuda.synchronize()
+    ms, st, c, wk, rf = decode_block(moe, wz, xz, yz, steps, 2, stream_gbps)
+    moe.pack(dense=wdev.upload_dense(wz, s))
+    torch.cuda.synchronize()
+    target = wz.T * s.k / s.E
+    q = {"calibration_tokens": wz.T, "m": int(np.floor(target + 0.5)), "count_target_Tk_over_E": target,
+         "calibration_ms": cal_ms,
+         "admitted_per_expert_min_max": [int(admitted.min()), int(admitted.max())],
+         "before": {"expert_load": load_summary(counts_before), "rank_max_over_mean": rank_loads(counts_before)},
+         "after": {"expert_load": load_summary(c), "rank_max_over_mean": rank_loads(c), "ms_per_step": ms,
+                   "layer_hbm_gbps": wk.layer_bytes / (ms * 1e-3) / 1e9, "stages_ms": st},
+         "experts_within_2x_of_target": float(((c >= target / 2) & (c <= 2 * target)).mean())}
+    log(f"[bench] quantile balancing (T={wz.T}, m={q['m']}): expert max/mean "
+        f"{q['before']['expert_load']['max_over_mean']:.2f} -> {q['after']['expert_load']['max_over_mean']:.2f}, "
+        f"active {q['before']['expert_load']['n_active']} -> {q['after']['expert_load']['n_active']}, "
+        f"rank max/mean {q['before']['rank_max_over_mean']:.2f} -> {q['after']['rank_max_over_mean']:.2f}, "
+        f"{ms:.4f} ms/step")
+    return q
 
 
 def ep_rank(moe, prov, wl, x, steps, stream_gbps, n_ranks=8, rank=0):

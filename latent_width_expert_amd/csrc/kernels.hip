@@ -659,7 +659,8 @@ __device__ __forceinline__ void barrier_nowait() { asm volatile("s_barrier" ::: 
 // one wave's MFMAs run while the other waits on LDS or on its DMA issues. Per K window of 128, by
 // LDS-DMA (buffer_load ... lds) issued from asm:
 //   - the chunk's activation rows (MXFP8: E4M3 codes and E8M0 scales) into an A stage shared by all
-//     waves, DA windows ahead (16-byte chunk c of row r stored at position c ^ (r & 7));
+//     waves, DA windows ahead (16-byte chunk c of row r stored at position c ^ (r mod CPR), CPR the
+//     row's chunks: the 16 rows of a tile read one chunk each from 16 different bank groups);
 //   - each panel-window of weights into a B stage, DB windows ahead, non-temporal (the weights
 //     come from HBM, the activation rows mostly from L2).
 // Nothing in the loop is a compiler-visible global load: one explicit vmcnt wait and a barrier per
@@ -679,6 +680,7 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
   constexpr int MTW = MT / NPH;                 // row tiles per wave
   constexpr int AROW = MX ? 128 : 256;          // bytes of a row's K window
   constexpr int CPR = AROW / 16;                // 16-byte chunks per row
+  constexpr int SWZ = CPR - 1;                  // row bits of the chunk swizzle
   constexpr int RPD = 1024 / AROW;              // rows per 1 KB code DMA
   constexpr int ESZ = MX ? 1 : 2;               // bytes per activation element
   constexpr int A_SC = ROWS * AROW;
@@ -780,7 +782,7 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
     wr = sgpr_rsrc(args.W + (DENSE ? 0 : (int64_t)grp * args.w_group_stride) + (int64_t)panel0 * nwin * kPanelWinBytes,
                    (int64_t)npan * nwin * kPanelWinBytes);
       // A DMAs of this wave: code instruction j = wv APW + jj covers chunk rows RPD j .. RPD j + RPD - 1
-      // (lane L: row RPD j + L / CPR, position L % CPR holding 16-byte chunk (L % CPR) ^ (row & 7) of
+      // (lane L: row RPD j + L / CPR, position L % CPR holding 16-byte chunk (L % CPR) ^ (row & SWZ) of
       // the row's window); MXFP8: the scale instruction covers rows 64 wv .. 64 wv + 63 (lane L: row
       // 64 wv + L; waves past the chunk's rows send theirs to the sink). Rows past the chunk and
       // elements past K read zeros.
@@ -796,7 +798,7 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
       #pragma unroll
       for (int jj = 0; jj < APW; ++jj) {
         const int r = RPD * (wv * APW + jj) + lane / CPR;
-        const int c = (lane % CPR) ^ (r & 7);
+        const int c = (lane % CPR) ^ (r & SWZ);
         akel[jj] = 16 * c / ESZ;  // first K element of the chunk inside the window
         acode[jj] = mb + r < r1 ? acode[jj] * (int)args.lda * ESZ + 16 * c : -1;
       }
@@ -1000,13 +1002,13 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
           auto load_tile = [&](int j, ATileT& aop, int& asc) {  // the wave's j-th tile: row tile h + NPH j
             const uint8_t* pr = prow + j * NPH * 16 * AROW;
             if constexpr (MX) {
-              const u32x4 lo = *(const u32x4*)(pr + 16 * (g ^ (i16 & 7)));
-              const u32x4 hi = *(const u32x4*)(pr + 16 * ((4 + g) ^ (i16 & 7)));
+              const u32x4 lo = *(const u32x4*)(pr + 16 * (g ^ (i16 & SWZ)));
+              const u32x4 hi = *(const u32x4*)(pr + 16 * ((4 + g) ^ (i16 & SWZ)));
               asc = psc[j * NPH * 64];
               aop = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
             } else {
               #pragma unroll
-              for (int st = 0; st < 4; ++st) aop[st] = *(const u32x4*)(pr + 16 * ((4 * g + st) ^ (i16 & 7)));
+              for (int st = 0; st < 4; ++st) aop[st] = *(const u32x4*)(pr + 16 * ((4 * g + st) ^ (i16 & SWZ)));
               asc = 0;
             }
           };
@@ -1115,10 +1117,10 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int NWAVE, int DA, int DB, int EPI, int TAG>
+template <int NWAVE, int MT, int DA, int DB, int EPI, int TAG>
 __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(NWAVE / 4, NWAVE / 4)))
 void tiled_f8_kernel(GemmArgs args) {
-  constexpr int MT = 12, ROWS = 16 * MT, NPG = 4, NPH = NWAVE / NPG, MTW = MT / NPH;
+  constexpr int ROWS = 16 * MT, NPG = 4, NPH = NWAVE / NPG, MTW = MT / NPH;
   constexpr int AROW = 128, A_SC = ROWS * AROW, A_STAGE = A_SC + ROWS * 4;
   constexpr int NB = DB + 1;
   constexpr int APL = ROWS * AROW / (16 * 64 * NWAVE);  // 16-byte activation pieces per lane and window
@@ -1474,12 +1476,13 @@ __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmArgs args) {
   const u32 lds_s = lds_addr(&lds_sink[wv][0]);
 
   // activation DMA jj of this wave covers rows RPD (wv APW + jj) .. + RPD - 1 (lane L: row + L / CPR,
-  // position L % CPR holding chunk (L % CPR) ^ (row & 7)); rows past M read zeros
+  // position L % CPR holding chunk (L % CPR) ^ (row & 15): a tile's 16 rows read 16 bank groups); rows
+  // past M read zeros
   int acode[APW], akel[APW];
 #pragma unroll
   for (int jj = 0; jj < APW; ++jj) {
     const int r = RPD * (wv * APW + jj) + lane / CPR;
-    const int c = (lane % CPR) ^ (r & 7);
+    const int c = (lane % CPR) ^ (r & 15);
     akel[jj] = 8 * c;
     acode[jj] = r < args.M ? r * (int)args.lda * 2 + 16 * c : -1;
   }
@@ -1572,7 +1575,7 @@ __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmArgs args) {
       // row tile t, lane (i16, g), MFMA step st = 2 kh + s: K elements [32 g + 8 st, +8); the next
       // step's operands are read from LDS while this step's MFMAs run
       auto aload = [&](int t, int s) {
-        return *(const u32x4*)(prow + t * 16 * AROW + 16 * ((4 * g + 2 * kh + s) ^ (i16 & 7)));
+        return *(const u32x4*)(prow + t * 16 * AROW + 16 * ((4 * g + 2 * kh + s) ^ i16));
       };
       u32x4 a_cur[NT];
 #pragma unroll
@@ -1777,15 +1780,15 @@ static void launch_f8(const GemmArgs& a, hipStream_t s) {
     launch_grouped_tiled<3, 2, 12, EPI, TAG, A_MXFP8>(a, s);
   } else {
     // gate/up: 192-row chunks on 8 waves, weights 2 windows ahead in registers, activation rows 2 ahead
-    constexpr int NW = 8, DB = 2, DA = 2;
+    constexpr int NW = 8, MT = 12, DB = 2, DA = 2;
     const unsigned nblk = (unsigned)ceil_div(a.P, 4);
     unsigned grid = (unsigned)ceil_div(a.n_groups, 8) * 8 * nblk;
     if (a.items) {
       hipLaunchKernelGGL(tile_items_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.n_groups, a.row_split, a.row_cap,
-                         192, (int)nblk, a.items);
+                         16 * MT, (int)nblk, a.items);
       grid = kItemGrid;
     }
-    hipLaunchKernelGGL((tiled_f8_kernel<NW, DA, DB, EPI, TAG>), dim3(grid), dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((tiled_f8_kernel<NW, MT, DA, DB, EPI, TAG>), dim3(grid), dim3(64 * NW), 0, s, a);
   }
 }
 
