@@ -299,3 +299,32 @@ WORKLOADS = {
 
 def get(name: str) -> Workload:
     return WORKLOADS[name]
+
+
+def fingerprint(wl: Workload) -> dict:
+    """sha256 of a workload's canonical inputs (bf16 bit patterns, MX codes and scales as stored): the
+    whole x batch, the router bias, the dense matrices, every shared expert, the first and last routed
+    expert (and their LoRA factors). A change of the generator or of a seed shows here."""
+    import hashlib
+    s = wl.shape
+
+    def h(*arrays):
+        d = hashlib.sha256()
+        for a in arrays:
+            a = np.ascontiguousarray(a)
+            d.update(str((a.dtype.str, a.shape)).encode())
+            d.update(a.tobytes())
+        return d.hexdigest()
+
+    out = {"x": h(wl.x_bits()), "router_bias": h(wl.router_bias()), "w_router": h(*wl.w_router())}
+    if s.latent_moe:
+        out["w_down"] = h(*wl.w_down())
+        out["w_up"] = h(*wl.w_up())
+    for j in range(s.Ns):
+        out[f"shared{j}"] = h(*(a for m in wl.shared(j) for a in m))
+    for e in sorted({0, s.E - 1}):
+        out[f"expert{e}"] = h(*(a for m in wl.routed(e) for a in m))
+        if s.lora_rank:
+            lo = wl.lora(e)
+            out[f"lora{e}"] = h(*(lo[n] for n in LORA_NAMES))
+    return out
