@@ -310,7 +310,7 @@ __device__ __forceinline__ void lora_add(const GemmArgs& args, f32x4& acc, int g
 
 // Epilogue of one 16-row tile (rows mb .. mb + 15, valid below r1) of one panel of group grp.
 __device__ __forceinline__ void epilogue(const GemmArgs& args, const f32x4 (&acc_in)[4], int panel, int mb, int r1,
-                                         int lane, int grp) {
+                                         int lane, int grp, bool lora_done = false) {
   int si = 0;
   for (int s = 0; s < args.nseg; ++s)
     if (panel >= args.seg[s].p0 && panel < args.seg[s].p1) si = s;
@@ -319,7 +319,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& args, const f32x4 (&acc
   const int pl = panel - sg.p0;
   const int mode = sg.mode;
   f32x4 acc[4] = {acc_in[0], acc_in[1], acc_in[2], acc_in[3]};
-  if (args.lora_t) {
+  if (args.lora_t && !lora_done) {
     if (mode == EPI_SWIGLU_BF16 || mode == EPI_SWIGLU_MXFP8) {
       // row-tiles: gate and up of units 32 pl + j, then of units 32 pl + 16 + j
       const int R = args.lora_rank;
@@ -417,8 +417,14 @@ struct BlockShape {
 // AHEAD: A tiles travel in the weight ring (prefetched NBUF - 1 windows ahead, few rows per
 // wave); otherwise each window's A tile is loaded just before the next weight prefetch (MT
 // tiles of A would not fit the ring), so waiting for it never waits for that prefetch.
-template <int KSPLIT, int AFMT, int NBUF, int MT, bool AHEAD, int TAG>
+// LR > 0 (grouped launches with BF16 LoRA deltas of rank at most LR): the delta of the tile is
+// added to the accumulators by fp32 MFMA 16x16x4 steps before the epilogue, with lane group g
+// taking rank indices [g LR/4, (g + 1) LR/4) on both operands; its operands (the tile's rows of
+// t = A v and the panel's columns of B) are loaded before the window loop, so their latency hides
+// behind the weight stream instead of following it.
+template <int KSPLIT, int AFMT, int NBUF, int MT, bool AHEAD, int LR, int TAG>
 __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_kernel(GemmArgs args) {
+  static_assert(LR == 0 || (MT == 1 && KSPLIT == 1 && LR % 16 == 0 && LR <= 32), "LoRA tiles");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps the resources scalar
   int pblock, grp = 0, r0, r1;
@@ -473,6 +479,69 @@ __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_ker
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) acc[mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // LoRA operands of this tile (LR > 0): lt[qg][s] = t[row][qg rank + g LS + s] for the lane's A
+    // row (qg 1: the up half of a GLU's t), lb[ct][s] = B[col][q0 + g LS + s] for the lane's column
+    // of row-tile ct (bf16 pairs); lane groups past the rank hold zeros.
+    constexpr int LS = LR > 0 ? LR / 4 : 2;
+    constexpr bool GLU = TAG == GEMM_GATEUP;
+    [[maybe_unused]] f32x4 lt[2][LS / 4 > 0 ? LS / 4 : 1];
+    [[maybe_unused]] u32 lb[4][LS / 2];
+    auto lora_loads = [&]() {
+      if constexpr (LR > 0) {
+        const int rank = args.lora_rank;
+        const bool gok = (g + 1) * LS <= rank;
+        const int row = mb + (lane & 15);
+#pragma unroll
+        for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+          for (int v = 0; v < LS / 4; ++v) lt[qg][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (gok && row < r1) {
+          const float* tp = args.lora_t + (int64_t)row * args.lora_ldt + g * LS;
+#pragma unroll
+          for (int qg = 0; qg < (GLU ? 2 : 1); ++qg)
+#pragma unroll
+            for (int v = 0; v < LS / 4; ++v) lt[qg][v] = *(const f32x4*)(tp + qg * rank + 4 * v);
+        }
+        const int j = lane & 15;
+        const uint16_t* bb = args.lora_b + (int64_t)grp * args.lora_b_stride + g * LS;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int col = GLU ? 32 * panel + 16 * (ct >> 1) + j : 64 * panel + 16 * ct + j;
+          const int q0 = GLU && (ct & 1) ? rank : 0;
+          const bool ok = gok && panel_ok && col < args.seg[0].ncols;
+#pragma unroll
+          for (int v = 0; v < LS / 2; ++v) lb[ct][v] = 0u;
+          if (ok) {
+            const uint16_t* bp = bb + (int64_t)col * args.lora_ldb + q0;
+            if constexpr (LS == 4) {
+              const uint2 w2 = *(const uint2*)bp;
+              lb[ct][0] = w2.x;
+              lb[ct][1] = w2.y;
+            } else {
+              static_assert(LS == 8, "rank classes 16 and 32");
+              const u32x4 w4 = *(const u32x4*)bp;
+#pragma unroll
+              for (int v = 0; v < 4; ++v) lb[ct][v] = w4[v];
+            }
+          }
+        }
+      }
+    };
+    auto lora_mfma = [&]() {
+      if constexpr (LR > 0) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int qg = GLU ? (ct & 1) : 0;
+#pragma unroll
+          for (int st = 0; st < LS; ++st) {
+            const u32 w = lb[ct][st / 2];
+            const float bv = __uint_as_float(st % 2 ? (w & 0xFFFF0000u) : (w << 16));
+            acc[0][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(lt[qg][st / 4][st % 4], bv, acc[0][ct], 0, 0, 0);
+          }
+        }
+      }
+    };
+
     // Loads are issued unconditionally: past the range they return zeros without memory traffic.
     auto load_tile = [&](AWin<AFMT>(&at)[MT], int wi) {
       const int kb = wi < nwin ? 4 * (wbeg + wi) + g : (1 << 24);
@@ -486,6 +555,7 @@ __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_ker
         load_w(buf[i].w, wr, lane, i);
         load_tile(buf[i].a, i);
       }
+      lora_loads();
       for (int w0 = 0; w0 < nwin; w0 += NBUF) {
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
@@ -499,6 +569,7 @@ __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_ker
       WWin wb[NBUF];
 #pragma unroll
       for (int i = 0; i < NBUF - 1; ++i) load_w(wb[i], wr, lane, i);
+      lora_loads();
       for (int w0 = 0; w0 < nwin; w0 += NBUF) {
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
@@ -530,6 +601,7 @@ __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_ker
         __syncthreads();
       }
     }
+    lora_mfma();
     if (panel_ok && ks == 0) {
       for (int mt = 0; mt < MT && mb + 16 * mt < r1; ++mt) {
         // copy tile mt out with static indices (the loop itself stays rolled)
@@ -540,7 +612,7 @@ __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_ker
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) tile[rt] = acc[m2][rt];
           }
-        epilogue(args, tile, panel, mb + 16 * mt, r1, lane, grp);
+        epilogue(args, tile, panel, mb + 16 * mt, r1, lane, grp, LR > 0);
       }
     }
   }
@@ -735,6 +807,16 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
     cpanel0 = 4 * (xcd + 8 * (slot / ngrp));
     cgrp = slot % ngrp;
     if (cpanel0 >= args.P) return;
+    cmb = cgrp * ROWS;
+    cr1 = min(cmb + ROWS, args.M);
+  } else if (DENSE && ngrp >= 8) {
+    // chunk c on XCD c mod 8 (its activation rows stay in that L2); the XCD's chunks are taken G at a
+    // time with their panel blocks interleaved, so the blocks in flight share each weight panel G ways
+    const int G = max(1, args.chunk_group);
+    const int gi = slot / (G * nblk), within = slot % (G * nblk);
+    cgrp = xcd + 8 * (gi * G + within % G);
+    cpanel0 = 4 * (within / G);
+    if (cgrp >= ngrp) return;
     cmb = cgrp * ROWS;
     cr1 = min(cmb + ROWS, args.M);
   } else {
@@ -1673,7 +1755,7 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs args, int G
   epilogue(args, acc, panel, 16 * t, min(args.M, kSkinnyRows), lane, 0);
 }
 
-template <int KSPLIT, int AFMT, int NBUF, int MT, bool AHEAD, int TAG>
+template <int KSPLIT, int AFMT, int NBUF, int MT, bool AHEAD, int TAG, int LR = 0>
 static void launch_one(GemmArgs a, hipStream_t s) {
   constexpr int ppb = BlockShape<KSPLIT>::panels;
   const int pblocks = (int)ceil_div(a.P, ppb);
@@ -1684,8 +1766,20 @@ static void launch_one(GemmArgs a, hipStream_t s) {
     a.m_passes = (int)ceil_div(a.M, 16 * MT);
     grid = dim3((unsigned)(ceil_div(pblocks, 8) * 8 * a.m_passes));
   }
-  hipLaunchKernelGGL((panel_gemm_kernel<KSPLIT, AFMT, NBUF, MT, AHEAD, TAG>), grid, dim3(64 * BlockShape<KSPLIT>::waves),
-                     0, s, a);
+  hipLaunchKernelGGL((panel_gemm_kernel<KSPLIT, AFMT, NBUF, MT, AHEAD, LR, TAG>), grid,
+                     dim3(64 * BlockShape<KSPLIT>::waves), 0, s, a);
+}
+
+// Grouped panel launches: with LoRA deltas the instance whose rank class holds the rank (the deltas
+// then go in by MFMA steps inside the kernel), otherwise the plain one.
+template <int AFMT, int NBUF, int TAG>
+static void launch_grouped_panel(const GemmArgs& a, hipStream_t s) {
+  if (!a.lora_t)
+    launch_one<1, AFMT, NBUF, 1, true, TAG>(a, s);
+  else if (a.lora_rank <= 16)
+    launch_one<1, AFMT, NBUF, 1, true, TAG, 16>(a, s);
+  else
+    launch_one<1, AFMT, NBUF, 1, true, TAG, 32>(a, s);
 }
 
 // Grouped launches split their groups by row count (row_split): the row-tiled kernel takes the groups
@@ -1811,6 +1905,7 @@ static void launch_bf16_grouped(const GemmArgs& a, hipStream_t s) {
 // aligned. With 1024 rows or more: 128-row chunks (at least 8, one XCD each); fewer: 64-row chunks
 // with the weights 4 windows ahead (few chunks: the kernel is mostly a weight stream).
 constexpr int kDenseRows = 128;
+constexpr int kDenseChunkGroup = 1;
 static bool dense_tiled_ok(const GemmArgs& a) {
   return !a.offsets && a.a_fmt == A_BF16 && a.M > 0 && a.lda % 8 == 0 && a.K % 32 == 0 &&
          a.a_bytes < ((int64_t)1 << 31) - (1 << 24);
@@ -1821,9 +1916,13 @@ static void launch_dense_tiled(const GemmArgs& a, hipStream_t s) {
   constexpr int WPS = 2, PPW = 1;
   const unsigned nblk = (unsigned)ceil_div(a.P, 4);
   if (a.M >= 8 * kDenseRows) {
-    const unsigned g8 = (unsigned)ceil_div(ceil_div(a.M, kDenseRows), 8) * 8;
-    hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, true, 2, 2, kDenseRows / 16, WPS, PPW, 2, TAG>), dim3(g8 * nblk),
-                       dim3(256 * WPS), 0, s, a);
+    // 128-row chunks, chunk first, kDenseChunkGroup chunks of an XCD at a time
+    GemmArgs b = a;
+    b.panel_major = 0;
+    b.chunk_group = kDenseChunkGroup;
+    const unsigned per_xcd = (unsigned)ceil_div(ceil_div(ceil_div(a.M, kDenseRows), 8), kDenseChunkGroup) * kDenseChunkGroup;
+    hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, true, 2, 2, kDenseRows / 16, WPS, PPW, 2, TAG>),
+                       dim3(8 * per_xcd * nblk), dim3(256 * WPS), 0, s, b);
   } else {
     // 64-row chunks, panel-major: the grid covers every (panel block, chunk), XCD by XCD
     GemmArgs b = a;
@@ -1893,13 +1992,13 @@ hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) 
         pa.row_split = 0;
       }
       if (gu && bf)
-        launch_one<1, A_BF16, 4, 1, true, GEMM_GATEUP>(pa, s);  // weights 3 windows ahead
+        launch_grouped_panel<A_BF16, 4, GEMM_GATEUP>(pa, s);  // weights 3 windows ahead
       else if (gu)
-        launch_one<1, A_MXFP8, 3, 1, true, GEMM_GATEUP>(pa, s);
+        launch_grouped_panel<A_MXFP8, 3, GEMM_GATEUP>(pa, s);
       else if (bf)
-        launch_one<1, A_BF16, 3, 1, true, GEMM_DOWN>(pa, s);
+        launch_grouped_panel<A_BF16, 3, GEMM_DOWN>(pa, s);
       else
-        launch_one<1, A_MXFP8, 3, 1, true, GEMM_DOWN>(pa, s);
+        launch_grouped_panel<A_MXFP8, 3, GEMM_DOWN>(pa, s);
       break;
     }
     default:
@@ -2386,9 +2485,13 @@ __device__ __forceinline__ void lora_act_load(const LoraAArgs& a, rsrc_t ar, rsr
   }
 }
 
+// One block of kLoraWaves waves per group; the K windows are dealt over the waves, each wave keeping the
+// next window's weights (and its first row tile's activations) in flight while it computes the current
+// one; the waves' partial sums are added in wave order through LDS (deterministic). NCT column tiles of 16.
 constexpr int kLoraWaves = 4;
+template <int NCT>
 __global__ __launch_bounds__(64 * kLoraWaves) void lora_a_kernel(LoraAArgs a) {
-  __shared__ f32x4 red[kLoraWaves][4][64];  // one row tile's partial sums of every wave
+  __shared__ f32x4 red[kLoraWaves][NCT][64];  // one row tile's partial sums of every wave
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = blockIdx.x;
@@ -2396,17 +2499,20 @@ __global__ __launch_bounds__(64 * kLoraWaves) void lora_a_kernel(LoraAArgs a) {
   if (r0 >= r1) return;  // uniform
   const int i16 = lane & 15, g = lane >> 4;
   const int nwin = (a.K + kWinK - 1) / kWinK;
-  const int nct = (a.N + 15) / 16;
   const rsrc_t ar = make_rsrc(a.A, a.a_bytes);
   const rsrc_t asr = make_rsrc(a.A_scales, a.A_scales ? a.as_bytes : 0);
   const rsrc_t lr = make_rsrc(a.La + (int64_t)grp * a.la_stride, (int64_t)a.N * a.K * 2);
+  struct Win {
+    bf16x8 b[NCT][4];
+    bf16x8 a0[4];
+  };
   for (int mb = r0; mb < r1; mb += 64) {
     const int nrt = min(4, (r1 - mb + 15) / 16);
-    f32x4 acc[4][4];
+    f32x4 acc[4][NCT];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     int arow[4];
     bool aok[4];
 #pragma unroll
@@ -2415,37 +2521,51 @@ __global__ __launch_bounds__(64 * kLoraWaves) void lora_a_kernel(LoraAArgs a) {
       aok[rt] = rt < nrt && row < r1;
       arow[rt] = aok[rt] ? (a.rowmap ? a.rowmap[row] : row) : 0;
     }
-    for (int w = wv; w < nwin; w += kLoraWaves) {
+    auto load_win = [&](Win& x, int w) {
       const int kb = 4 * w + g;
-      bf16x8 bv[4][4];
+      const bool win = w < nwin && kb * 32 < a.K;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
+      for (int ct = 0; ct < NCT; ++ct) {
         const int n = 16 * ct + i16;
-        const int off = ct < nct && n < a.N && kb * 32 < a.K ? (n * a.K + kb * 32) * 2 : kOOB;
+        const int off = win && n < a.N ? (n * a.K + kb * 32) * 2 : kOOB;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) bv[ct][st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(lr, off + 16 * st, 0, 0));
+        for (int st = 0; st < 4; ++st)
+          x.b[ct][st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(lr, off + 16 * st, 0, 0));
       }
+      lora_act_load(a, ar, asr, arow[0], aok[0] && w < nwin, kb, x.a0);
+    };
+    Win cur, nxt;
+    load_win(cur, wv);
+    for (int w = wv; w < nwin; w += kLoraWaves) {
+      load_win(nxt, w + kLoraWaves);
+      const int kb = 4 * w + g;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         if (rt < nrt) {  // uniform
           bf16x8 av[4];
-          lora_act_load(a, ar, asr, arow[rt], aok[rt], kb, av);
+          if (rt == 0) {
+#pragma unroll
+            for (int st = 0; st < 4; ++st) av[st] = cur.a0[st];
+          } else {
+            lora_act_load(a, ar, asr, arow[rt], aok[rt], kb, av);
+          }
 #pragma unroll
           for (int st = 0; st < 4; ++st)
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-              if (ct < nct) acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[st], bv[ct][st], acc[rt][ct], 0, 0, 0);
+            for (int ct = 0; ct < NCT; ++ct)
+              acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[st], cur.b[ct][st], acc[rt][ct], 0, 0, 0);
         }
       }
+      cur = nxt;
     }
     // the waves' partial sums, one row tile at a time, added in wave order (deterministic)
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       if (rt < nrt) {  // uniform
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) red[wv][ct][lane] = acc[rt][ct];
+        for (int ct = 0; ct < NCT; ++ct) red[wv][ct][lane] = acc[rt][ct];
         __syncthreads();
-        if (wv < nct) {  // wave ct adds column tile ct
+        if (wv < NCT) {  // wave ct adds column tile ct
           const int ct = wv;
           f32x4 v = red[0][ct][lane];
           for (int q = 1; q < kLoraWaves; ++q) v += red[q][ct][lane];
@@ -2466,7 +2586,13 @@ __global__ __launch_bounds__(64 * kLoraWaves) void lora_a_kernel(LoraAArgs a) {
 hipError_t launch_lora_a(const LoraAArgs& a, hipStream_t s) {
   if (a.n_groups <= 0) return hipSuccess;
   if (a.N < 8 || a.N > 64 || a.N % 8 || a.K % 32 || a.K <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(lora_a_kernel, dim3((unsigned)a.n_groups), dim3(64 * kLoraWaves), 0, s, a);
+  const dim3 grid((unsigned)a.n_groups), block(64 * kLoraWaves);
+  switch ((a.N + 15) / 16) {
+    case 1: hipLaunchKernelGGL(lora_a_kernel<1>, grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL(lora_a_kernel<2>, grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL(lora_a_kernel<3>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(lora_a_kernel<4>, grid, block, 0, s, a); break;
+  }
   return hipGetLastError();
 }
 
