@@ -406,6 +406,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& args, const f32x4 (&acc
   }
 }
 
+// Workgroup barrier after this wave's LDS operations have completed, without waiting for its
+// outstanding global loads (a weight ring in flight stays in flight); also a compiler memory barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only: this wave's LDS writes and reads are done
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // Waves per block: KSPLIT waves per panel, 4 panels per block when KSPLIT == 1.
 template <int KSPLIT>
 struct BlockShape {
@@ -422,9 +429,16 @@ struct BlockShape {
 // taking rank indices [g LR/4, (g + 1) LR/4) on both operands; its operands (the tile's rows of
 // t = A v and the panel's columns of B) are loaded before the window loop, so their latency hides
 // behind the weight stream instead of following it.
-template <int KSPLIT, int AFMT, int NBUF, int MT, bool AHEAD, int LR, int TAG>
+// ASH (grouped launches of up to 16 rows per expert, several rows each): the four waves of a block (one
+// expert, four panels) share the expert's 16-row A tile: each wave loads a quarter of the window's tile
+// into its ring, writes it to one of two LDS stages the window it is used, and after one barrier every
+// wave reads its operands from there (16-byte chunk c of row r at position c ^ r, conflict-free).
+// A costs one load per lane and window instead of four, which leaves the weight stream more of the
+// per-CU load path.
+template <int KSPLIT, int AFMT, int NBUF, int MT, bool AHEAD, int LR, bool ASH, int TAG>
 __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_kernel(GemmArgs args) {
   static_assert(LR == 0 || (MT == 1 && KSPLIT == 1 && LR % 16 == 0 && LR <= 32), "LoRA tiles");
+  static_assert(!ASH || (MT == 1 && KSPLIT == 1 && LR == 0), "shared A tiles");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps the resources scalar
   int pblock, grp = 0, r0, r1;
@@ -452,16 +466,21 @@ __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_ker
 
   const int wbeg = (args.wwin * ks) / KSPLIT;
   const int wend = (args.wwin * (ks + 1)) / KSPLIT;
-  const int nwin = panel_ok ? wend - wbeg : 0;
+  // with a shared A tile every wave of the block runs every window (the barriers), a wave past the
+  // last panel on a weight resource of no bytes
+  const int nwin = (ASH || panel_ok) ? wend - wbeg : 0;
   const rsrc_t wr = make_rsrc(args.W + (int64_t)grp * args.w_group_stride +
                                   ((int64_t)(panel_ok ? panel : 0) * args.wwin + wbeg) * kPanelWinBytes,
-                              (int64_t)nwin * kPanelWinBytes);
+                              (int64_t)(panel_ok ? nwin : 0) * kPanelWinBytes);
   const rsrc_t ar = make_rsrc(args.A, args.a_bytes);
   const rsrc_t asr = make_rsrc(args.A_scales, args.A_scales ? args.as_bytes : 0);
   const int g = lane >> 4;
 
   // partial sums of the upper half of the K-split waves, per tree level
   __shared__ f32x4 red[KSPLIT > 1 ? (KSPLIT / 2) * MT * 4 * 64 : 1];
+  // shared A tile stages: bf16 16 rows x 256 bytes; MXFP8 16 rows x 128 bytes of codes + 16 scale words
+  constexpr int ASTG = AFMT == A_BF16 ? 4096 : 2048 + 64;
+  __shared__ __attribute__((aligned(16))) uint8_t ash[ASH ? 2 : 1][ASH ? ASTG : 16];
 
   for (int mb = r0; mb < r1; mb += 16 * MT) {
     bool rv[MT];
@@ -548,7 +567,85 @@ __global__ __launch_bounds__(64 * BlockShape<KSPLIT>::waves) void panel_gemm_ker
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) load_a<AFMT>(at[mt], ar, asr, args, arow[mt], rv[mt], kb);
     };
-    if constexpr (AHEAD) {
+    if constexpr (ASH) {
+      // this lane's piece of the block's tile: bf16, 16-byte chunk pc of row pr (256 pieces, every lane
+      // of the 4 waves); MXFP8, chunk pc of row pr for the 128 lanes of waves 0 and 1, and the row's
+      // scale word (4 K blocks) for lanes 0..15 of wave 2
+      const int pi = 64 * wave + lane;
+      const int pr = AFMT == A_BF16 ? pi >> 4 : (wave < 2 ? pi >> 3 : (wave == 2 ? lane : 16));
+      const int pc = AFMT == A_BF16 ? pi & 15 : pi & 7;
+      const bool pv = pr < 16 && mb + pr < r1 && (AFMT == A_BF16 || wave < 2 || (wave == 2 && lane < 16));
+      const int parow = pv ? (args.rowmap ? args.rowmap[mb + pr] : mb + pr) : 0;
+      struct SBuf {
+        WWin w;
+        u32x4 p;
+      };
+      // pieces past K (a K tail inside the last window) read zeros, like the per-wave loads
+      auto load_piece = [&](SBuf& b, int wi) {
+        const bool in = pv && wi < nwin;
+        const int k0 = kWinK * (wbeg + wi);  // first K element of the window
+        if constexpr (AFMT == A_BF16) {
+          const int off = in && k0 + 8 * pc < args.K ? (parow * (int)args.lda + k0 + 8 * pc) * 2 : kOOB;
+          b.p = __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0);
+        } else if (wave < 2) {
+          const int off = in && k0 + 16 * pc < args.K ? parow * (int)args.lda + k0 + 16 * pc : kOOB;
+          b.p = __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0);
+        } else {
+          u32 w = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int kb = k0 / 32 + q;
+            w |= (u32)__builtin_amdgcn_raw_buffer_load_b8(asr, in && 32 * kb < args.K ? parow * (int)args.ldas + kb : kOOB,
+                                                          0, 0) << (8 * q);
+          }
+          b.p = u32x4{w, 0u, 0u, 0u};
+        }
+      };
+      auto store_piece = [&](const SBuf& b, int stage) {
+        uint8_t* st = &ash[stage][0];
+        if constexpr (AFMT == A_BF16) {
+          *(u32x4*)(st + 256 * pr + 16 * (pc ^ pr)) = b.p;
+        } else if (wave < 2) {
+          *(u32x4*)(st + 128 * pr + 16 * (pc ^ (pr & 7))) = b.p;
+        } else if (wave == 2 && lane < 16) {
+          *(u32*)(st + 2048 + 4 * pr) = b.p[0];
+        }
+      };
+      auto read_tile = [&](AWin<AFMT>& at, int stage) {
+        const uint8_t* st = &ash[stage][0];
+        const int i16 = lane & 15;
+        if constexpr (AFMT == A_BF16) {
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) at.v[s2] = *(const u32x4*)(st + 256 * i16 + 16 * ((4 * g + s2) ^ i16));
+        } else {
+          at.v[0] = *(const u32x4*)(st + 128 * i16 + 16 * ((2 * g) ^ (i16 & 7)));
+          at.v[1] = *(const u32x4*)(st + 128 * i16 + 16 * ((2 * g + 1) ^ (i16 & 7)));
+          at.sc = st[2048 + 4 * i16 + g];
+        }
+      };
+      SBuf buf[NBUF];
+#pragma unroll
+      for (int i = 0; i < NBUF - 1; ++i) {
+        load_w(buf[i].w, wr, lane, i);
+        load_piece(buf[i], i);
+      }
+      for (int w0 = 0; w0 < nwin; w0 += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+          SBuf& nb = buf[(u + NBUF - 1) % NBUF];
+          load_w(nb.w, wr, lane, w0 + u + NBUF - 1);
+          load_piece(nb, w0 + u + NBUF - 1);
+          if (w0 + u < nwin) {  // uniform over the block
+            // stage (w & 1) was last read in window w - 2, before every wave reached the barrier of w - 1
+            store_piece(buf[u], (w0 + u) & 1);
+            lds_barrier();
+            AWin<AFMT> at[1];
+            read_tile(at[0], (w0 + u) & 1);
+            compute_window<AFMT, 1>(acc, buf[u].w, at);
+          }
+        }
+      }
+    } else if constexpr (AHEAD) {
       WinBuf<AFMT, MT> buf[NBUF];
 #pragma unroll
       for (int i = 0; i < NBUF - 1; ++i) {
@@ -1194,10 +1291,6 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
 // the current unit's epilogue.
 // EPI 0: fp32 out. EPI 1: GLU panels, SiLU(gate) * up MX-encoded (E4M3, E8M0 per 32 units), staged in
 // LDS and written as 16-byte row segments.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only: this wave's LDS writes and reads are done
-  asm volatile("s_barrier" ::: "memory");
-}
 
 template <int NWAVE, int MT, int DA, int DB, int EPI, int TAG>
 __global__ __launch_bounds__(64 * NWAVE) __attribute__((amdgpu_waves_per_eu(NWAVE / 4, NWAVE / 4)))
@@ -1755,7 +1848,7 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs args, int G
   epilogue(args, acc, panel, 16 * t, min(args.M, kSkinnyRows), lane, 0);
 }
 
-template <int KSPLIT, int AFMT, int NBUF, int MT, bool AHEAD, int TAG, int LR = 0>
+template <int KSPLIT, int AFMT, int NBUF, int MT, bool AHEAD, int TAG, int LR = 0, bool ASH = false>
 static void launch_one(GemmArgs a, hipStream_t s) {
   constexpr int ppb = BlockShape<KSPLIT>::panels;
   const int pblocks = (int)ceil_div(a.P, ppb);
@@ -1766,15 +1859,20 @@ static void launch_one(GemmArgs a, hipStream_t s) {
     a.m_passes = (int)ceil_div(a.M, 16 * MT);
     grid = dim3((unsigned)(ceil_div(pblocks, 8) * 8 * a.m_passes));
   }
-  hipLaunchKernelGGL((panel_gemm_kernel<KSPLIT, AFMT, NBUF, MT, AHEAD, LR, TAG>), grid,
+  hipLaunchKernelGGL((panel_gemm_kernel<KSPLIT, AFMT, NBUF, MT, AHEAD, LR, ASH, TAG>), grid,
                      dim3(64 * BlockShape<KSPLIT>::waves), 0, s, a);
 }
 
+// The shared A tile for experts of up to 16 rows when some experts have more (several rows each);
+// kPanelSharedAFew: also when every expert is small (decode, about one row each).
+constexpr bool kPanelSharedAFew = false;
 // Grouped panel launches: with LoRA deltas the instance whose rank class holds the rank (the deltas
 // then go in by MFMA steps inside the kernel), otherwise the plain one.
 template <int AFMT, int NBUF, int TAG>
 static void launch_grouped_panel(const GemmArgs& a, hipStream_t s) {
-  if (!a.lora_t)
+  if (!a.lora_t && (a.row_split > 1 || kPanelSharedAFew))
+    launch_one<1, AFMT, NBUF, 1, true, TAG, 0, true>(a, s);  // several rows per expert: one A tile per block
+  else if (!a.lora_t)
     launch_one<1, AFMT, NBUF, 1, true, TAG>(a, s);
   else if (a.lora_rank <= 16)
     launch_one<1, AFMT, NBUF, 1, true, TAG, 16>(a, s);
