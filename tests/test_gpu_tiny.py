@@ -171,7 +171,8 @@ def check_all(name, T):
 @pytest.mark.parametrize("name", ["tiny", "tiny_mxfp8", "tiny_mxfp8_many", "tiny_mxfp8_deep", "tiny_dense_many",
                                   "tiny_fullwidth", "tiny_skewed", "tiny_bf16_many", "tiny_bf16_deep", "tiny_split",
                                   "tiny_split_mxfp8", "tiny_e12_mxfp8", "tiny_e4_bf16", "tiny_lora",
-                                  "tiny_lora_mxfp8_many", "tiny_lora_bf16_many", "tiny_lora_split"])
+                                  "tiny_lora_mxfp8_many", "tiny_lora_bf16_many", "tiny_lora_split",
+                                  "tiny_lora_r32_skewed", "tiny_lora_mxfp8_r8"])
 def test_full_parity(name):
     check_all(name, workloads.get(name).T)
 
@@ -179,6 +180,12 @@ def test_full_parity(name):
 @pytest.mark.parametrize("T", [1, 3, 16, 17, 40, 63])
 def test_ragged_token_counts(T):
     check_all("tiny", T)
+
+
+@pytest.mark.parametrize("T", [1, 17, 31])
+def test_lora_ragged(T):
+    """LoRA deltas on the panel kernel at ragged batch sizes (one row to two row tiles per expert)."""
+    check_all("tiny_lora", T)
 
 
 def test_mxfp8_ragged():

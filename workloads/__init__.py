@@ -268,6 +268,15 @@ WORKLOADS = {
                                                                       lora_rank=32), T=512, seed=14,
                                     note="tiny layer, bf16, rank-32 LoRA, 128 rows per expert (bf16 row-tiled "
                                          "kernels)"),
+    "tiny_lora_r32_skewed": Workload("tiny_lora_r32_skewed", LayerShape(d=256, l=128, h=96, E=16, k=4, Ns=1, hs=96,
+                                                                        lora_rank=32), T=31, seed=15, bias="zipf",
+                                     zipf_alpha=1.5,
+                                     note="tiny layer, rank-32 LoRA, literal Zipf bias: hot experts of more than 16 "
+                                          "rows on the panel kernel (two row tiles)"),
+    "tiny_lora_mxfp8_r8": Workload("tiny_lora_mxfp8_r8", LayerShape(d=256, l=128, h=96, E=16, k=4, Ns=1, hs=96,
+                                                                    act="mxfp8", lora_rank=8), T=40, seed=16,
+                                   note="tiny layer, MXFP8, rank-8 LoRA, 10 rows per expert (panel and row-tiled "
+                                        "kernels in one stage)"),
     "tiny_lora_split": Workload("tiny_lora_split", LayerShape(d=256, l=128, h=128, E=16, k=2, Ns=1, hs=96,
                                                               lora_rank=16), T=128, seed=9, bias="zipf",
                                 zipf_alpha=0.3,
