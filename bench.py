@@ -13,7 +13,8 @@ The same run also measures, each on its own resident layer (one at a time):
               the decode and the prefill shapes
   lora        the decode batch with rank-16 BF16 LoRA deltas on every routed expert matrix
   prefill     T = 8192 with MXFP8 latent and hidden activations
-  fullwidth   the conventional top-8 MoE at width 7168, T = 64 and T = 2048
+  fullwidth   the conventional top-8 MoE at width 7168, T = 64 and T = 2048, with the LatentMoE layer at
+              T = 2048 (bf16 activations) as its partner at the same dispatch payload
 and the plain HBM read rate of a streaming kernel (k3moe_stream_read) as the practical ceiling.
 
 Prints one JSON line: tokens/s, the roofline of the dominant kernel (the grouped gate/up GEMM, HBM-
@@ -423,8 +424,27 @@ def main():
                                "fullwidth_ms": fw["t64"]["ms_per_step"],
                                "fullwidth_bytes": fw["t64"]["layer_algorithmic_bytes"],
                                "speedup": fw["t64"]["ms_per_step"] / ms_step}
-        out["fullwidth"] = fw
         del fm
+        gpu_gc()
+        # the LatentMoE partner at T = 2048 (K3 shape, bf16 activations, every expert active)
+        wk3 = workloads.get("k3_t2048")
+        km = wdev.build_layer(wk3, wk3.shape, max_tokens=wk3.T, verbose=False)
+        xk = wdev.x_tensor(wk3)
+        yk = torch.empty_like(xk)
+        ms, st, c, wkk, rf = decode_block(km, wk3, xk, yk, sec_steps, 2, stream_gbps)
+        fw["latent_t2048"] = {"workload": wk3.name, "tokens": wk3.T, "top_k": wk3.shape.k, "ms_per_step": ms,
+                              "tokens_per_s": wk3.T / (ms * 1e-3), "layer_algorithmic_bytes": wkk.layer_bytes,
+                              "layer_hbm_gbps": wkk.layer_bytes / (ms * 1e-3) / 1e9, "gateup": rf, "stages_ms": st,
+                              "active_experts": wkk.n_active, "expert_load": load_summary(c),
+                              "dispatch_values_per_token": wk3.shape.k * wk3.shape.expert_in}
+        fw["vs_latent_t2048"] = {"latent_ms": ms, "latent_bytes": wkk.layer_bytes,
+                                 "fullwidth_ms": fw["t2048"]["ms_per_step"],
+                                 "fullwidth_bytes": fw["t2048"]["layer_algorithmic_bytes"],
+                                 "speedup": fw["t2048"]["ms_per_step"] / ms}
+        log(f"[bench] latent T=2048 (bf16): {ms:.3f} ms/step, {wkk.layer_bytes / 1e9:.2f} GB; full width "
+            f"{fw['vs_latent_t2048']['speedup']:.2f}x slower")
+        out["fullwidth"] = fw
+        del km, xk, yk
         gpu_gc()
 
     res = {

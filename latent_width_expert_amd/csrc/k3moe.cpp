@@ -322,6 +322,7 @@ static int run_experts(k3moe_ctx* ctx, const void* A, const uint8_t* A_scales, i
     a.offsets = offsets;
     a.n_groups = E;
     a.row_split = row_split;
+    a.M = (int32_t)R;  // rows over every group (the launcher picks kernels by rows per group)
     a.items = B.items;
     EpiSeg& sg = a.seg[0];
     sg.p0 = 0;
@@ -386,6 +387,7 @@ static int run_experts(k3moe_ctx* ctx, const void* A, const uint8_t* A_scales, i
     a.offsets = offsets;
     a.n_groups = E;
     a.row_split = row_split;
+    a.M = (int32_t)R;  // rows over every group (the launcher picks kernels by rows per group)
     a.items = B.items;
     EpiSeg& sg = a.seg[0];
     sg.p0 = 0;

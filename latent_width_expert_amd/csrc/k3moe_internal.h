@@ -94,7 +94,7 @@ struct GemmArgs {
   const int32_t* rowmap;   // optional: output row -> A row
   const int32_t* offsets;  // grouped: rows of group g are [offsets[g], offsets[g+1])
   int32_t n_groups;        // grouped: number of groups
-  int32_t M;               // dense: rows
+  int32_t M;               // dense: rows; grouped: rows over every group (0: unknown)
   int32_t m_passes;        // dense: row passes (set by the launcher)
   int32_t row_split;       // grouped: 0 = the panel kernel takes every group; 1 = the row-tiled kernel takes
                            // every group; n > 1 = groups of at least n rows take the row-tiled kernel and

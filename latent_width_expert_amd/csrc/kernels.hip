@@ -1863,9 +1863,176 @@ static void launch_one(GemmArgs a, hipStream_t s) {
                      dim3(64 * BlockShape<KSPLIT>::waves), 0, s, a);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Grouped GEMM for experts of a few tens of rows (between the decode weight stream and the row-tiled
+// prefill tiles): the panel kernel's weight stream with up to MT 16-row tiles of A per pass.
+// Block: 4 waves on one expert and 4 consecutive panels, wave p computing panel 4 pblock + p. Per 128-K
+// window each wave takes its panel-window from a register ring (NBUF - 1 windows ahead, non-temporal;
+// the lane's 16 bytes are its operand, converted once to bf16 and used by every tile) and a share of
+// the expert's A rows (MT tiles; bf16: MT pieces of 16 bytes a lane; MXFP8: codes for waves 0 and 1,
+// scale words for wave 2) in the same ring; the shares go to one of two LDS stages the window they are
+// used (16-byte chunk c of tile row r at position c ^ r) and after one barrier every wave reads its
+// operands from there. Only tiles holding rows issue MFMAs. Experts with rows in [row_split, row_cap)
+// run here; the others return at once.
+// ---------------------------------------------------------------------------------------------
+template <int AFMT, int NBUF, int MT, int TAG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void panel_rows_kernel(GemmArgs args) {
+  constexpr int TB = AFMT == A_BF16 ? 4096 : 2048;  // code bytes of one 16-row tile's window
+  constexpr int ASTG = MT * (TB + (AFMT == A_BF16 ? 0 : 64));
+  __shared__ __attribute__((aligned(16))) uint8_t ash[2][ASTG];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pblock = blockIdx.x, grp = blockIdx.y;
+  const int r0 = args.offsets[grp], r1 = args.offsets[grp + 1];
+  if (r1 - r0 < max(args.row_split, 1) || r1 - r0 >= args.row_cap || 4 * pblock >= args.P) return;  // uniform
+  const int panel = 4 * pblock + wave;
+  const bool panel_ok = panel < args.P;
+  const int nwin = args.wwin;  // every wave runs every window (the barriers)
+  const rsrc_t wr = make_rsrc(args.W + (int64_t)grp * args.w_group_stride + (int64_t)(panel_ok ? panel : 0) * nwin * kPanelWinBytes,
+                              (int64_t)(panel_ok ? nwin : 0) * kPanelWinBytes);
+  const rsrc_t ar = make_rsrc(args.A, args.a_bytes);
+  const rsrc_t asr = make_rsrc(args.A_scales, args.A_scales ? args.as_bytes : 0);
+  const int g = lane >> 4, i16 = lane & 15;
+  // the lane's piece of each tile: bf16, chunk pc of row pr (all 256 lanes); MXFP8, chunk pc of row pr
+  // for waves 0 and 1, the row's scale word for lanes 0..15 of wave 2
+  const int pi = 64 * wave + lane;
+  const int pr = AFMT == A_BF16 ? pi >> 4 : (wave < 2 ? pi >> 3 : (wave == 2 ? lane : 16));
+  const int pc = AFMT == A_BF16 ? pi & 15 : pi & 7;
+  const bool plane = pr < 16 && (AFMT == A_BF16 || wave < 2 || (wave == 2 && lane < 16));
+  struct RB {
+    WWin w;
+    u32x4 p[MT];
+  };
+  for (int mb = r0; mb < r1; mb += 16 * MT) {
+    const int nt = min(MT, (r1 - mb + 15) / 16);  // tiles holding rows (uniform)
+    int parow[MT];
+    bool pv[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int row = mb + 16 * t + pr;
+      pv[t] = plane && t < nt && row < r1;
+      parow[t] = pv[t] ? (args.rowmap ? args.rowmap[row] : row) : 0;
+    }
+    f32x4 acc[MT][4];
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[t][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // pieces past K (a K tail inside the last window) read zeros
+    auto load_rb = [&](RB& b, int wi) {
+      load_w(b.w, wr, lane, wi);
+      const bool in = wi < nwin;
+      const int k0 = kWinK * wi;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        if constexpr (AFMT == A_BF16) {
+          const int off = in && pv[t] && k0 + 8 * pc < args.K ? (parow[t] * (int)args.lda + k0 + 8 * pc) * 2 : kOOB;
+          b.p[t] = __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0);
+        } else if (wave < 2) {
+          const int off = in && pv[t] && k0 + 16 * pc < args.K ? parow[t] * (int)args.lda + k0 + 16 * pc : kOOB;
+          b.p[t] = __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0);
+        } else {
+          u32 w = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int kb = k0 / 32 + q;
+            w |= (u32)__builtin_amdgcn_raw_buffer_load_b8(
+                     asr, in && pv[t] && 32 * kb < args.K ? parow[t] * (int)args.ldas + kb : kOOB, 0, 0)
+                 << (8 * q);
+          }
+          b.p[t] = u32x4{w, 0u, 0u, 0u};
+        }
+      }
+    };
+    auto store_pieces = [&](const RB& b, int stage) {
+      uint8_t* st = &ash[stage][0];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        if (t < nt) {  // uniform
+          if constexpr (AFMT == A_BF16) {
+            *(u32x4*)(st + TB * t + 256 * pr + 16 * (pc ^ pr)) = b.p[t];
+          } else if (wave < 2) {
+            *(u32x4*)(st + TB * t + 128 * pr + 16 * (pc ^ (pr & 7))) = b.p[t];
+          } else if (wave == 2 && lane < 16) {
+            *(u32*)(st + MT * TB + 64 * t + 4 * pr) = b.p[t][0];
+          }
+        }
+      }
+    };
+    auto compute = [&](const WWin& w, int stage) {
+      const uint8_t* st = &ash[stage][0];
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        bf16x8 wv[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) wv[rt] = fp4_operand(w.c[rt][s2], e8m0_f32((w.sc >> (8 * rt)) & 0xFFu));
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          if (t < nt) {  // uniform
+            bf16x8 av;
+            if constexpr (AFMT == A_BF16) {
+              av = __builtin_bit_cast(bf16x8, *(const u32x4*)(st + TB * t + 256 * i16 + 16 * ((4 * g + s2) ^ i16)));
+            } else {
+              // the step's 8 codes: K [32 g + 8 s2, +8) of the row, in chunk 2 g + s2 / 2
+              const uint2 c8 = *(const uint2*)(st + TB * t + 128 * i16 + 16 * ((2 * g + s2 / 2) ^ (i16 & 7)) + 8 * (s2 & 1));
+              const float sc = e8m0_f32(st[MT * TB + 64 * t + 4 * i16 + g]);
+              u32x4 r;
+              r[0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.x, sc, false));
+              r[1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.x, sc, true));
+              r[2] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.y, sc, false));
+              r[3] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8.y, sc, true));
+              av = __builtin_bit_cast(bf16x8, r);
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) acc[t][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, wv[rt], acc[t][rt], 0, 0, 0);
+          }
+        }
+      }
+    };
+    RB buf[NBUF];
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) load_rb(buf[i], i);
+    for (int w0 = 0; w0 < nwin; w0 += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        load_rb(buf[(u + NBUF - 1) % NBUF], w0 + u + NBUF - 1);
+        if (w0 + u < nwin) {  // uniform over the block
+          // stage (w & 1) was last read in window w - 2, before every wave reached the barrier of w - 1
+          store_pieces(buf[u], (w0 + u) & 1);
+          lds_barrier();
+          compute(buf[u].w, (w0 + u) & 1);
+        }
+      }
+    }
+    // every wave done with the stages before the next pass writes them
+    lds_barrier();
+    if (panel_ok) {
+      for (int t = 0; t < nt; ++t) {
+        f32x4 tile[4];
+#pragma unroll
+        for (int t2 = 0; t2 < MT; ++t2)
+          if (t2 == t) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) tile[rt] = acc[t2][rt];
+          }
+        epilogue(args, tile, panel, mb + 16 * t, r1, lane, grp);
+      }
+    }
+  }
+}
+
 // The shared A tile for experts of up to 16 rows when some experts have more (several rows each);
 // kPanelSharedAFew: also when every expert is small (decode, about one row each).
 constexpr bool kPanelSharedAFew = false;
+// Experts of fewer than kMidRows rows (and at least the launch's row split) take panel_rows_kernel
+// when the launch has no LoRA deltas; the row-tiled kernels keep the larger ones.
+constexpr int kMidRows = 64;
+constexpr bool kMidPanel = true;
+template <int AFMT, int NBUF, int TAG>
+static void launch_panel_rows(const GemmArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((panel_rows_kernel<AFMT, NBUF, kMidRows / 16, TAG>), dim3((unsigned)ceil_div(a.P, 4), (unsigned)a.n_groups),
+                     dim3(256), 0, s, a);
+}
 // Grouped panel launches: with LoRA deltas the instance whose rank class holds the rank (the deltas
 // then go in by MFMA steps inside the kernel), otherwise the plain one.
 template <int AFMT, int NBUF, int TAG>
@@ -1995,7 +2162,7 @@ static void launch_bf16_grouped(const GemmArgs& a, hipStream_t s) {
   lo.row_cap = kBf16SmallRows;
   hi.row_split = std::max(a.row_split, kBf16SmallRows);
   hi.row_cap = 0;
-  launch_grouped_tiled<3, 4, 4, EPI, TAG, A_BF16>(lo, s);
+  if (a.row_split < kBf16SmallRows) launch_grouped_tiled<3, 4, 4, EPI, TAG, A_BF16>(lo, s);
   launch_grouped_tiled<2, 2, 8, EPI, TAG, A_BF16>(hi, s);
 }
 
@@ -2077,14 +2244,33 @@ hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) 
       const int mode = gu ? (bf ? EPI_SWIGLU_BF16 : EPI_SWIGLU_MXFP8) : EPI_F32;
       GemmArgs pa = a;  // the panel kernel's share
       if (tiled_grouped_ok(a, mode)) {
+        // without LoRA deltas: experts of [row_split, kMidRows) rows on panel_rows_kernel, larger ones
+        // on the row-tiled kernels
+        // (not when the average group holds 2 kMidRows rows or more: groups below kMidRows are then rare
+        // and a launch of one block per (panel block, group) that mostly returns at once costs more)
+        const bool mid = kMidPanel && !a.lora_t && (a.M <= 0 || a.M < (int64_t)2 * kMidRows * a.n_groups);
+        GemmArgs ta = a;
+        if (mid) {
+          ta.row_split = std::max(a.row_split, kMidRows);
+          GemmArgs ma = a;
+          ma.row_cap = kMidRows;
+          if (gu && bf)
+            launch_panel_rows<A_BF16, 3, GEMM_GATEUP>(ma, s);
+          else if (gu)
+            launch_panel_rows<A_MXFP8, 3, GEMM_GATEUP>(ma, s);
+          else if (bf)
+            launch_panel_rows<A_BF16, 3, GEMM_DOWN>(ma, s);
+          else
+            launch_panel_rows<A_MXFP8, 3, GEMM_DOWN>(ma, s);
+        }
         if (gu && bf)
-          launch_bf16_grouped<2, GEMM_GATEUP>(a, s);
+          launch_bf16_grouped<2, GEMM_GATEUP>(ta, s);
         else if (gu)
-          launch_f8<1, GEMM_GATEUP>(a, s);
+          launch_f8<1, GEMM_GATEUP>(ta, s);
         else if (bf)
-          launch_bf16_grouped<0, GEMM_DOWN>(a, s);
+          launch_bf16_grouped<0, GEMM_DOWN>(ta, s);
         else
-          launch_f8<0, GEMM_DOWN>(a, s);
+          launch_f8<0, GEMM_DOWN>(ta, s);
         if (a.row_split == 1) break;  // no group left for the panel kernel
       } else {
         pa.row_split = 0;
