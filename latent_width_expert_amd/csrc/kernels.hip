@@ -2028,6 +2028,7 @@ constexpr bool kPanelSharedAFew = false;
 // when the launch has no LoRA deltas; the row-tiled kernels keep the larger ones.
 constexpr int kMidRows = 64;
 constexpr bool kMidPanel = true;
+constexpr bool kMidTakesSmall = false;
 template <int AFMT, int NBUF, int TAG>
 static void launch_panel_rows(const GemmArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((panel_rows_kernel<AFMT, NBUF, kMidRows / 16, TAG>), dim3((unsigned)ceil_div(a.P, 4), (unsigned)a.n_groups),
@@ -2254,6 +2255,7 @@ hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) 
           ta.row_split = std::max(a.row_split, kMidRows);
           GemmArgs ma = a;
           ma.row_cap = kMidRows;
+          if (kMidTakesSmall) ma.row_split = 1;  // the panel kernel's experts too (no launch of its own)
           if (gu && bf)
             launch_panel_rows<A_BF16, 3, GEMM_GATEUP>(ma, s);
           else if (gu)
@@ -2271,7 +2273,7 @@ hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) 
           launch_bf16_grouped<0, GEMM_DOWN>(ta, s);
         else
           launch_f8<0, GEMM_DOWN>(ta, s);
-        if (a.row_split == 1) break;  // no group left for the panel kernel
+        if (a.row_split == 1 || (mid && kMidTakesSmall)) break;  // no group left for the panel kernel
       } else {
         pa.row_split = 0;
       }
