@@ -129,28 +129,34 @@ def roofline_of(kernel, bytes_, flops, ms, peak_tflops, traffic=None, stream_gbp
 
 def time_forward(moe, x, y, steps, warmup, profile=True):
     """Average ms per forward over `steps` timed calls (events on torch's current stream, the library
-    launches on it) and the library's per-stage averages over the same calls."""
+    launches on it), then -- with profile -- the library's per-stage averages over a second region of
+    the same number of calls (its stage events add small gaps between launches, so the step time is
+    taken without them). Returns (ms per step, stage averages, ms per step with the stage events)."""
     import torch
     for _ in range(warmup):
         moe.forward(x, y)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+
+    def region():
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(steps):
+            moe.forward(x, y)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / steps
+
+    ms = region()
+    stages, ms_prof = None, None
     if profile:
         moe.profile_begin(steps)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(steps):
-        moe.forward(x, y)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    total = ev0.elapsed_time(ev1)
-    stages = None
-    if profile:
+        ms_prof = region()
         sm, calls = moe.profile_end()
         assert calls == steps
         stages = {k: v / calls for k, v in sm.items()}
-    return total / steps, stages
+    return ms, stages, ms_prof
 
 
 def time_call(fn, steps, warmup):
@@ -245,13 +251,14 @@ def decode_block(moe, wl, x, y, steps, warmup, stream_gbps):
     """Time one decode-like workload on a packed layer; its figures."""
     s = wl.shape
     T = x.shape[0]
-    ms, stages = time_forward(moe, x, y, steps, warmup)
+    ms, stages, ms_prof = time_forward(moe, x, y, steps, warmup)
     counts = counts_of(moe, x, y, s.E)
     w = Work(s, T, counts)
     gu = stages["gateup"]
-    return ms, stages, counts, w, roofline_of("gateup (grouped GLU gate/up GEMM, MXFP4 weight stream)", w.gu_bytes,
-                                              w.gu_flops, gu, w.routed_peak, recorded_traffic(wl.name, "gateup"),
-                                              stream_gbps)
+    rf = roofline_of("gateup (grouped GLU gate/up GEMM, MXFP4 weight stream)", w.gu_bytes, w.gu_flops, gu,
+                     w.routed_peak, recorded_traffic(wl.name, "gateup"), stream_gbps)
+    rf["step_ms_with_stage_events"] = ms_prof  # the region the stage durations come from
+    return ms, stages, counts, w, rf
 
 
 def main():
