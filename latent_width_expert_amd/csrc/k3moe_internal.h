@@ -100,7 +100,7 @@ struct GemmArgs {
                            // every group; n > 1 = groups of at least n rows take the row-tiled kernel and
                            // the others the panel kernel (both launched; each skips the other's groups)
   int32_t row_cap;         // grouped, row-tiled kernel: when > 0, groups of row_cap or more rows are left to
-                           // another row-tiled launch (set by the launcher)
+                           // another launch; mid-row kernel: its groups have fewer (set by the launcher)
   int32_t panel_major;     // dense, row-tiled kernel: blocks dealt panel block first (set by the launcher)
   int32_t chunk_group;     // dense, row-tiled kernel, chunk first: chunks of an XCD taken this many at a time
                            // with their panel blocks interleaved (set by the launcher; 0 or 1: one chunk)

@@ -225,6 +225,15 @@ def test_split_by_rows_ragged(name, T):
     check_all(name, T)
 
 
+@pytest.mark.parametrize("name", ["tiny_e4_all", "tiny_e4_all_mxfp8"])
+@pytest.mark.parametrize("T", [15, 16, 17, 63, 64, 65, 127, 128])
+def test_row_band_boundaries(name, T):
+    """Every token chooses every one of the 4 experts, so each expert has exactly T rows: 15 rows (panel
+    kernel), 16, 17 and 63 (mid-row kernel, one to four tiles), 64 and more (row-tiled kernels), and the
+    switch that leaves the mid-row kernel unlaunched (T k = 128 E)."""
+    check_all(name, T)
+
+
 @pytest.mark.parametrize("T", [700, 1024, 1500])
 def test_dense_many_rows_ragged(T):
     """Row-tiled dense GEMMs with a partial last chunk: 64-row chunks dealt panel block first (T = 700),

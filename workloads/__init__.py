@@ -249,6 +249,12 @@ WORKLOADS = {
                                note="tiny layer, MXFP8, 12 experts (XCD classes of unequal size), many rows"),
     "tiny_e4_bf16": Workload("tiny_e4_bf16", LayerShape(d=256, l=128, h=128, E=4, k=2, Ns=1, hs=96), T=256,
                              seed=11, note="tiny layer, bf16, 4 experts (XCD classes without experts), many rows"),
+    "tiny_e4_all": Workload("tiny_e4_all", LayerShape(d=256, l=128, h=96, E=4, k=4, Ns=1, hs=96), T=128, seed=17,
+                            note="tiny layer, bf16, 4 experts each chosen by every token: the batch size sets every "
+                                 "expert's row count exactly (kernel band boundaries), K tail in the down GEMM"),
+    "tiny_e4_all_mxfp8": Workload("tiny_e4_all_mxfp8", LayerShape(d=256, l=128, h=128, E=4, k=4, Ns=1, hs=96,
+                                                                  act="mxfp8"), T=128, seed=18,
+                                  note="as tiny_e4_all with MXFP8 latent and hidden activations"),
     "tiny_dense_many": Workload("tiny_dense_many", LayerShape(d=256, l=128, h=96, E=16, k=4, Ns=1, hs=96), T=2048,
                                 seed=8, note="tiny layer, bf16, 2048 tokens (row-tiled dense GEMMs, K tail "
                                              "in the latent/shared GEMM)"),
