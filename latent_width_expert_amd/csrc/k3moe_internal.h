@@ -102,8 +102,6 @@ struct GemmArgs {
   int32_t row_cap;         // grouped, row-tiled kernel: when > 0, groups of row_cap or more rows are left to
                            // another launch; mid-row kernel: its groups have fewer (set by the launcher)
   int32_t panel_major;     // dense, row-tiled kernel: blocks dealt panel block first (set by the launcher)
-  int32_t chunk_group;     // dense, row-tiled kernel, chunk first: chunks of an XCD taken this many at a time
-                           // with their panel blocks interleaved (set by the launcher; 0 or 1: one chunk)
   int32_t* items;          // grouped, row-tiled kernel: workspace of tile_items_bytes() for the work-item
                            // list (persistent grid); null: one block per (group, panel block)
   int32_t nseg;

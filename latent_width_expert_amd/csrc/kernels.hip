@@ -906,16 +906,6 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
     if (cpanel0 >= args.P) return;
     cmb = cgrp * ROWS;
     cr1 = min(cmb + ROWS, args.M);
-  } else if (DENSE && ngrp >= 8) {
-    // chunk c on XCD c mod 8 (its activation rows stay in that L2); the XCD's chunks are taken G at a
-    // time with their panel blocks interleaved, so the blocks in flight share each weight panel G ways
-    const int G = max(1, args.chunk_group);
-    const int gi = slot / (G * nblk), within = slot % (G * nblk);
-    cgrp = xcd + 8 * (gi * G + within % G);
-    cpanel0 = 4 * (within / G);
-    if (cgrp >= ngrp) return;
-    cmb = cgrp * ROWS;
-    cr1 = min(cmb + ROWS, args.M);
   } else {
     const bool spread = ngrp < 8;
     cgrp = spread ? (int)blockIdx.x / nblk : xcd + 8 * (slot / nblk);
@@ -2021,14 +2011,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// The shared A tile for experts of up to 16 rows when some experts have more (several rows each);
-// kPanelSharedAFew: also when every expert is small (decode, about one row each).
-constexpr bool kPanelSharedAFew = false;
 // Experts of fewer than kMidRows rows (and at least the launch's row split) take panel_rows_kernel
 // when the launch has no LoRA deltas; the row-tiled kernels keep the larger ones.
 constexpr int kMidRows = 64;
-constexpr bool kMidPanel = true;
-constexpr bool kMidTakesSmall = false;
 template <int AFMT, int NBUF, int TAG>
 static void launch_panel_rows(const GemmArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((panel_rows_kernel<AFMT, NBUF, kMidRows / 16, TAG>), dim3((unsigned)ceil_div(a.P, 4), (unsigned)a.n_groups),
@@ -2038,7 +2023,7 @@ static void launch_panel_rows(const GemmArgs& a, hipStream_t s) {
 // then go in by MFMA steps inside the kernel), otherwise the plain one.
 template <int AFMT, int NBUF, int TAG>
 static void launch_grouped_panel(const GemmArgs& a, hipStream_t s) {
-  if (!a.lora_t && (a.row_split > 1 || kPanelSharedAFew))
+  if (!a.lora_t && a.row_split > 1)  // some experts have several rows: the shared A tile
     launch_one<1, AFMT, NBUF, 1, true, TAG, 0, true>(a, s);  // several rows per expert: one A tile per block
   else if (!a.lora_t)
     launch_one<1, AFMT, NBUF, 1, true, TAG>(a, s);
@@ -2171,7 +2156,6 @@ static void launch_bf16_grouped(const GemmArgs& a, hipStream_t s) {
 // aligned. With 1024 rows or more: 128-row chunks (at least 8, one XCD each); fewer: 64-row chunks
 // with the weights 4 windows ahead (few chunks: the kernel is mostly a weight stream).
 constexpr int kDenseRows = 128;
-constexpr int kDenseChunkGroup = 1;
 static bool dense_tiled_ok(const GemmArgs& a) {
   return !a.offsets && a.a_fmt == A_BF16 && a.M > 0 && a.lda % 8 == 0 && a.K % 32 == 0 &&
          a.a_bytes < ((int64_t)1 << 31) - (1 << 24);
@@ -2182,13 +2166,12 @@ static void launch_dense_tiled(const GemmArgs& a, hipStream_t s) {
   constexpr int WPS = 2, PPW = 1;
   const unsigned nblk = (unsigned)ceil_div(a.P, 4);
   if (a.M >= 8 * kDenseRows) {
-    // 128-row chunks, chunk first, kDenseChunkGroup chunks of an XCD at a time
+    // 128-row chunks, chunk first (chunk c on XCD c mod 8, its activation rows read from that L2)
     GemmArgs b = a;
     b.panel_major = 0;
-    b.chunk_group = kDenseChunkGroup;
-    const unsigned per_xcd = (unsigned)ceil_div(ceil_div(ceil_div(a.M, kDenseRows), 8), kDenseChunkGroup) * kDenseChunkGroup;
-    hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, true, 2, 2, kDenseRows / 16, WPS, PPW, 2, TAG>),
-                       dim3(8 * per_xcd * nblk), dim3(256 * WPS), 0, s, b);
+    const unsigned g8 = (unsigned)ceil_div(ceil_div(a.M, kDenseRows), 8) * 8;
+    hipLaunchKernelGGL((tiled_gemm_kernel<A_BF16, true, 2, 2, kDenseRows / 16, WPS, PPW, 2, TAG>), dim3(g8 * nblk),
+                       dim3(256 * WPS), 0, s, b);
   } else {
     // 64-row chunks, panel-major: the grid covers every (panel block, chunk), XCD by XCD
     GemmArgs b = a;
@@ -2249,13 +2232,12 @@ hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) 
         // on the row-tiled kernels
         // (not when the average group holds 2 kMidRows rows or more: groups below kMidRows are then rare
         // and a launch of one block per (panel block, group) that mostly returns at once costs more)
-        const bool mid = kMidPanel && !a.lora_t && (a.M <= 0 || a.M < (int64_t)2 * kMidRows * a.n_groups);
+        const bool mid = !a.lora_t && (a.M <= 0 || a.M < (int64_t)2 * kMidRows * a.n_groups);
         GemmArgs ta = a;
         if (mid) {
           ta.row_split = std::max(a.row_split, kMidRows);
           GemmArgs ma = a;
           ma.row_cap = kMidRows;
-          if (kMidTakesSmall) ma.row_split = 1;  // the panel kernel's experts too (no launch of its own)
           if (gu && bf)
             launch_panel_rows<A_BF16, 3, GEMM_GATEUP>(ma, s);
           else if (gu)
@@ -2273,7 +2255,7 @@ hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) 
           launch_bf16_grouped<0, GEMM_DOWN>(ta, s);
         else
           launch_f8<0, GEMM_DOWN>(ta, s);
-        if (a.row_split == 1 || (mid && kMidTakesSmall)) break;  // no group left for the panel kernel
+        if (a.row_split == 1) break;  // no group left for the panel kernel
       } else {
         pa.row_split = 0;
       }
