@@ -886,9 +886,9 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
   const u32 lds_s = lds_addr(&lds_sink[0]);
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   // Work units. Grouped launches with an item list: a persistent grid (a multiple of 8 blocks) whose
-  // blocks walk the list of their XCD, one item (expert, chunk of ROWS rows, panel block) at a time
-  // (tile_items_kernel; the experts of XCD x are those with e mod 8 = x, so their rows are re-read
-  // from that L2). Otherwise one block per (group, panel block): eight groups or more, group g on
+  // blocks walk the run of their XCD, one item (expert, chunk of ROWS rows, panel block) at a time
+  // (tile_items_kernel: equal contiguous runs, so an expert's rows and weights stay in one or two
+  // XCDs' L2). Otherwise one block per (group, panel block): eight groups or more, group g on
   // XCD g mod 8; fewer, the panel blocks of each group dealt over all XCDs (block b: group b / nblk).
   const bool listed = !DENSE && args.items != nullptr;
   int it = 0, it_end = 0, it_step = 1;
@@ -2049,10 +2049,14 @@ static bool tiled_grouped_ok(const GemmArgs& a, int mode) {
   return true;
 }
 
-// Work-item list of a grouped row-tiled launch (one block of 1024 threads): the experts taken in XCD
-// classes (class x: experts x, x + 8, ...), each contributing ceil(rows / ROWS) chunks x nblk panel
-// blocks if its row count is in [max(split, 1), cap) (cap 0: unbounded), in the order (expert,
-// chunk, panel block); out[x] = start of class x's items, out[8] = the total.
+// Work-item list of a grouped row-tiled launch (one block of 1024 threads): every expert whose row
+// count is in [max(split, 1), cap) (cap 0: unbounded) contributes ceil(rows / ROWS) chunks x nblk panel
+// blocks, listed in the order (expert, panel block, chunk); the list is cut into 8 equal contiguous
+// runs, run x for XCD x: out[x] = start of run x, out[8] = the total. Equal runs keep the XCDs equally
+// busy however the rows are spread over the experts (a few hot experts would otherwise load a few
+// XCDs), and contiguous runs keep each expert on one or two XCDs: the chunks of a panel block are
+// adjacent (its weights are read once per XCD) and an expert's panel blocks follow one another (its
+// activation rows stay in that L2).
 constexpr int kMinChunkRows = 64;
 int64_t tile_items_bytes(int64_t max_rows, int n_groups, int nblk) {
   return 4 * (kItemHeader + (int64_t)nblk * (n_groups + max_rows / kMinChunkRows + 1));
@@ -2061,11 +2065,10 @@ bool tile_items_fit(int64_t max_rows_per_group, int n_groups, int nblk) {
   return n_groups >= 1 && n_groups <= 2048 && nblk >= 1 && nblk <= 256 && max_rows_per_group / kMinChunkRows < 4095;
 }
 
-__device__ __forceinline__ int tile_items_of(const int32_t* offsets, int E, int per, int q, int split, int cap,
-                                             int rows, int nblk, int& e, int& nch) {
-  e = 8 * (q % per) + q / per;
+__device__ __forceinline__ int tile_items_of(const int32_t* offsets, int E, int e, int split, int cap, int rows, int nblk,
+                                             int& nch) {
   nch = 0;
-  if (q >= 8 * per || e >= E) return 0;
+  if (e >= E) return 0;
   const int c = offsets[e + 1] - offsets[e];
   if (c < max(split, 1) || (cap > 0 && c >= cap)) return 0;
   nch = (c + rows - 1) / rows;
@@ -2076,10 +2079,9 @@ __global__ __launch_bounds__(1024) void tile_items_kernel(const int32_t* __restr
                                                           int rows, int nblk, int32_t* __restrict__ out) {
   __shared__ int part[1024];
   const int t = threadIdx.x;
-  const int per = (E + 7) / 8;             // experts per XCD class
-  const int qpt = (8 * per + 1023) / 1024; // class positions per thread (q = x per + i: expert 8 i + x)
-  int sum = 0, e, nch;
-  for (int j = 0; j < qpt; ++j) sum += tile_items_of(offsets, E, per, t * qpt + j, split, cap, rows, nblk, e, nch);
+  const int ept = (E + 1023) / 1024;  // experts per thread: t ept .. t ept + ept - 1
+  int sum = 0, nch;
+  for (int j = 0; j < ept; ++j) sum += tile_items_of(offsets, E, t * ept + j, split, cap, rows, nblk, nch);
   part[t] = sum;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan over the threads
@@ -2089,16 +2091,15 @@ __global__ __launch_bounds__(1024) void tile_items_kernel(const int32_t* __restr
     __syncthreads();
   }
   int base = part[t] - sum;
-  for (int j = 0; j < qpt; ++j) {
-    const int q = t * qpt + j;
-    const int n = tile_items_of(offsets, E, per, q, split, cap, rows, nblk, e, nch);
-    if (q < 8 * per && q % per == 0) out[q / per] = base;
-    for (int ck = 0; ck < nch; ++ck)
-      for (int pb = 0; pb < nblk; ++pb)
-        out[kItemHeader + base + ck * nblk + pb] = (int32_t)((u32)e | ((u32)ck << 12) | ((u32)pb << 24));
+  for (int j = 0; j < ept; ++j) {
+    const int e = t * ept + j;
+    const int n = tile_items_of(offsets, E, e, split, cap, rows, nblk, nch);
+    for (int pb = 0; pb < nblk && n > 0; ++pb)
+      for (int ck = 0; ck < nch; ++ck)
+        out[kItemHeader + base + pb * nch + ck] = (int32_t)((u32)e | ((u32)ck << 12) | ((u32)pb << 24));
     base += n;
   }
-  if (t == 1023) out[8] = part[1023];
+  if (t < 9) out[t] = (int32_t)(((int64_t)t * part[1023]) / 8);
 }
 
 // A grouped row-tiled launch: with an item list, the list for this row band and chunk height, then
