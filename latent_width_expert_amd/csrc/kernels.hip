@@ -2724,26 +2724,23 @@ hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, int64_t n, hipStre
 // deltas over the 4-bit base). The first factor t = act La^T of a grouped stage (rank columns per
 // matrix); the second factor is added in the grouped GEMMs' epilogues (lora_add).
 // One block of 4 waves per group: the group's rows in chunks of 64 (4 row tiles of 16); wave w takes
-// K windows w, w + 4, ... of 128; per window, lane (i, g) holds K [128 w + 32 g, +32) of row / column i
-// and four bf16 MFMA 16x16x32 steps cover it. The waves' sums are added in wave order through LDS
-// (deterministic).
+// K windows w, w + 4, ... of 128; in MFMA step st of a window, lane (i, g) holds K [128 w + 32 st + 8 g,
+// +8) of row / column i (four bf16 MFMA 16x16x32 steps a window). The waves' sums are added in wave
+// order through LDS (deterministic).
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ void lora_act_load(const LoraAArgs& a, rsrc_t ar, rsrc_t asr, int arow, bool ok, int kb,
+__device__ __forceinline__ void lora_act_load(const LoraAArgs& a, rsrc_t ar, rsrc_t asr, int arow, bool ok, int w, int g,
                                               bf16x8 (&v)[4]) {
-  const bool in = ok && kb * 32 < a.K;
-  if (a.a_fmt == A_BF16) {
-    const int off = in ? (arow * (int)a.lda + kb * 32) * 2 : kOOB;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) v[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ar, off + 16 * st, 0, 0));
-  } else {
-    const int off = in ? arow * (int)a.lda + kb * 32 : kOOB;
-    const u32x4 c0 = __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0);
-    const u32x4 c1 = __builtin_amdgcn_raw_buffer_load_b128(ar, off + 16, 0, 0);
-    const float sc = e8m0_f32(__builtin_amdgcn_raw_buffer_load_b8(asr, in ? arow * (int)a.ldas + kb : kOOB, 0, 0));
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const u32 d0 = st < 2 ? c0[2 * st] : c1[2 * st - 4];
-      const u32 d1 = st < 2 ? c0[2 * st + 1] : c1[2 * st - 3];
+  for (int st = 0; st < 4; ++st) {
+    const int k0 = kWinK * w + 32 * st + 8 * g;  // the lane's 8 K elements of step st
+    const bool in = ok && k0 < a.K;
+    if (a.a_fmt == A_BF16) {
+      v[st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ar, in ? (arow * (int)a.lda + k0) * 2 : kOOB, 0, 0));
+    } else {
+      const int off = in ? arow * (int)a.lda + k0 : kOOB;
+      const u32 d0 = __builtin_amdgcn_raw_buffer_load_b32(ar, off, 0, 0);
+      const u32 d1 = __builtin_amdgcn_raw_buffer_load_b32(ar, off == kOOB ? kOOB : off + 4, 0, 0);
+      const float sc = e8m0_f32(__builtin_amdgcn_raw_buffer_load_b8(asr, in ? arow * (int)a.ldas + k0 / 32 : kOOB, 0, 0));
       u32x4 r;
       r[0] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, false));
       r[1] = __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, sc, true));
@@ -2790,24 +2787,25 @@ __global__ __launch_bounds__(64 * kLoraWaves) void lora_a_kernel(LoraAArgs a) {
       aok[rt] = rt < nrt && row < r1;
       arow[rt] = aok[rt] ? (a.rowmap ? a.rowmap[row] : row) : 0;
     }
+    // MFMA step st of window w: lane group g takes K elements [128 w + 32 st + 8 g, +8) on both operands,
+    // so one load instruction reads 64 contiguous bytes of each of its 16 rows
     auto load_win = [&](Win& x, int w) {
-      const int kb = 4 * w + g;
-      const bool win = w < nwin && kb * 32 < a.K;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const int n = 16 * ct + i16;
-        const int off = win && n < a.N ? (n * a.K + kb * 32) * 2 : kOOB;
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-          x.b[ct][st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(lr, off + 16 * st, 0, 0));
+        for (int st = 0; st < 4; ++st) {
+          const int k0 = kWinK * w + 32 * st + 8 * g;
+          const int off = w < nwin && n < a.N && k0 < a.K ? (n * a.K + k0) * 2 : kOOB;
+          x.b[ct][st] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(lr, off, 0, 0));
+        }
       }
-      lora_act_load(a, ar, asr, arow[0], aok[0] && w < nwin, kb, x.a0);
+      lora_act_load(a, ar, asr, arow[0], aok[0] && w < nwin, w, g, x.a0);
     };
     Win cur, nxt;
     load_win(cur, wv);
     for (int w = wv; w < nwin; w += kLoraWaves) {
       load_win(nxt, w + kLoraWaves);
-      const int kb = 4 * w + g;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         if (rt < nrt) {  // uniform
@@ -2816,7 +2814,7 @@ __global__ __launch_bounds__(64 * kLoraWaves) void lora_a_kernel(LoraAArgs a) {
 #pragma unroll
             for (int st = 0; st < 4; ++st) av[st] = cur.a0[st];
           } else {
-            lora_act_load(a, ar, asr, arow[rt], aok[rt], kb, av);
+            lora_act_load(a, ar, asr, arow[rt], aok[rt], w, g, av);
           }
 #pragma unroll
           for (int st = 0; st < 4; ++st)
