@@ -6,7 +6,8 @@ offsets, permutation and inverse (bit-exact), and the latent z at its quantisati
 or MXFP8 codes: strict against the oracle's encoder on the GPU's fp32 values, end to end
 against the oracle's own values, boundary codes counted).
 Outputs: the decode batch of 64 tokens whole (y, u, n and the shared hidden of every token against
-the oracle's forward); the skewed and full-width batches on 16 tokens spread through the batch; the
+the oracle's forward); the skewed, full-width and T = 2048 batches on 16 tokens spread through the
+batch, the skewed and T = 2048 ones also stage-wise on every row of experts from each kernel band; the
 prefill chunk stage-wise on every dispatched row of 64 experts spread over the id range (the
 hottest, ids above 512, a count that is not a multiple of the 192-row chunk) and end to end on 64
 tokens spread through the batch. Also the BF16 LoRA variant at decode and the expert-parallel split
@@ -210,9 +211,29 @@ def test_k3_expert_parallel_rank_decode():
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["k3_decode_t512_zipf", "k3_decode_t512_zipf_cal"])
 def test_k3_decode_t512_skewed(name):
-    g = check_layer(workloads.get(name), spread(512, 16, extra=(5,)), max_tokens=512)
+    """16 spread tokens end to end; stage-wise, every row of experts from each kernel band: below 16 rows
+    (panel kernel, shared A tile), 16-63 (mid-row kernel), 64 and more (row-tiled kernel)."""
+    wl = workloads.get(name)
+    g = check_layer(wl, spread(512, 16, extra=(5,)), max_tokens=512, rows=True)
     c = g["counts"]
     assert c.sum() == 512 * 16
+    experts = band_experts(c, 4)
+    wh, wo, rows = stagewise_experts(wl, g, experts)
+    _log(f"[k3] {name} stage-wise: experts {experts} (rows {[int(c[e]) for e in experts]}): hidden within "
+         f"{wh:.3f} x its bound, expert outputs rel L2 <= {wo:.2e}")
+
+
+def band_experts(c, n):
+    """Up to n experts from each row band of the grouped kernels (1-15, 16-63, 64 and more rows), the
+    smallest and largest of each band first."""
+    out = []
+    for lo, hi in ((1, 16), (16, 64), (64, 1 << 30)):
+        ids = [int(e) for e in np.argsort(c, kind="stable") if lo <= c[e] < hi]
+        if ids:
+            mid = ids[1:-1]
+            pick = [ids[0], ids[-1]] + mid[:: max(1, len(mid) // max(1, n - 2))][: max(0, n - 2)]
+            out += pick
+    return sorted(set(out))
 
 
 @pytest.mark.timeout(900)
@@ -301,8 +322,16 @@ def _rank_check(wl, rank, n_ranks=8):
 
 @pytest.mark.timeout(900)
 def test_k3_t2048_bf16():
-    """K3 shape, 2048 tokens, bf16 activations: every expert on the row-tiled grouped bf16 kernel."""
-    check_layer(workloads.get("k3_t2048"), spread(2048, 16))
+    """K3 shape, 2048 tokens, bf16 activations (20-56 rows per expert: the mid-row kernel, the larger
+    experts on the row-tiled kernel): 16 spread tokens end to end, every row of experts from each band
+    stage-wise."""
+    wl = workloads.get("k3_t2048")
+    g = check_layer(wl, spread(2048, 16), rows=True)
+    c = g["counts"]
+    experts = band_experts(c, 6)
+    wh, wo, rows = stagewise_experts(wl, g, experts)
+    _log(f"[k3] k3_t2048 stage-wise: experts {experts} (rows {[int(c[e]) for e in experts]}): hidden within "
+         f"{wh:.3f} x its bound, expert outputs rel L2 <= {wo:.2e}")
 
 
 @pytest.mark.timeout(900)
