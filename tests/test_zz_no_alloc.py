@@ -1,7 +1,8 @@
 """The entry point that allocates nothing (k3moe_forward_noalloc, the library's static device scratch
 in place of a workspace) against k3moe_forward with a workspace, through the C ABI: bit-identical
 outputs (the same kernels on the same inputs) on two calls in a row, the second with fewer tokens,
-and a batch whose workspace exceeds the scratch rejected before any device work."""
+and a batch whose workspace exceeds the scratch rejected before any device work. Tiny layers (bf16,
+MXFP8, LoRA) and the K3-shape decode batch."""
 from __future__ import annotations
 
 import sys
@@ -21,10 +22,12 @@ def _log(msg):
     print(msg, file=sys.__stderr__, flush=True)
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_mxfp8_many"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_mxfp8_many", "tiny_lora", "k3_decode_t64"])
 def test_noalloc_matches_forward(name):
+    """(k3_decode_t64: the K3-shape decode batch of 64 tokens, whose workspace fits the scratch.)"""
     wl = workloads.get(name)
-    moe = wdev.build_layer(ArrayWeights(wl), wl.shape, max_tokens=wl.T)
+    prov = wl if name.startswith("k3") else ArrayWeights(wl)
+    moe = wdev.build_layer(prov, wl.shape, max_tokens=wl.T)
     for T in (wl.T, wl.T // 2 - 3):
         x = wdev.x_tensor(wl, T)
         y_ref = moe.forward(x)
