@@ -253,18 +253,22 @@ __device__ __forceinline__ void compute_window(f32x4 (&acc)[MT][4], const WWin& 
 
 // Maximum over each 16-lane row of the wave with DPP moves (quad swaps, then half-row and row
 // mirrors): every lane of the row ends with the row maximum.
+// The values are magnitudes (>= 0), whose order is the order of their bit patterns as unsigned
+// integers: the maximum is taken on those (no float canonicalisation, and the DPP moves fold into the
+// integer max).
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
-  return v;
+  u32 b = __float_as_uint(v);
+  b = max(b, (u32)__builtin_amdgcn_mov_dpp((int)b, 0xB1, 0xF, 0xF, true));
+  b = max(b, (u32)__builtin_amdgcn_mov_dpp((int)b, 0x4E, 0xF, 0xF, true));
+  b = max(b, (u32)__builtin_amdgcn_mov_dpp((int)b, 0x141, 0xF, 0xF, true));
+  b = max(b, (u32)__builtin_amdgcn_mov_dpp((int)b, 0x140, 0xF, 0xF, true));
+  return __uint_as_float(b);
 }
 
 // MX encode a block of 32 values held as v0 (column j) and v1 (column 16 + j) by the 16 lanes of
 // one lane group; returns the E4M3 codes of v0, v1 and the E8M0 byte. All 64 lanes must call.
 __device__ __forceinline__ void mxfp8_block(float v0, float v1, u32& c0, u32& c1, u32& sbyte) {
-  const float amax = row16_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const float amax = row16_max(__uint_as_float(max(__float_as_uint(v0) & 0x7FFFFFFFu, __float_as_uint(v1) & 0x7FFFFFFFu)));
   const int e = mx_shared_exp(amax, 8);
   sbyte = amax == 0.0f ? 0u : (u32)(e + 127);  // an all-zero block: scale byte 0, codes +-0
   const float inv = e8m0_f32((u32)(127 - e));  // 2^-e
