@@ -1538,7 +1538,7 @@ void tiled_f8_kernel(GemmArgs args) {
             mxfp8_block(v0, v1, c0, c1, sb);
             stg[lr * 128 + 32 * pg + ej] = (uint8_t)c0;
             stg[lr * 128 + 32 * pg + 16 + ej] = (uint8_t)c1;
-            stg_sc[lr * 4 + pg] = (uint8_t)sb;  // the 16 lanes of the block agree
+            if (ej == 0) stg_sc[lr * 4 + pg] = (uint8_t)sb;  // the 16 lanes of the block agree
           }
           __builtin_amdgcn_sched_barrier(0);
         }
