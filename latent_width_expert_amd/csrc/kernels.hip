@@ -1167,80 +1167,91 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
           }
           // A operands: row tile t of the stage starts at t * 16 AROW (MXFP8 scales at A_SC + t * 64);
           // the swizzle depends on the row only through row % 8 = i16 % 8. MXFP8 lane (i16, g): K bytes
-          // [16 g, +16) and [64 + 16 g, +16); bf16 lane (i16, g), step s: K elements [32 g + 8 s, +8).
+          // [16 g, +16) and [64 + 16 g, +16); bf16 lane (i16, g), MFMA step s: K elements [32 g + 8 s, +8).
           const uint8_t* sa = lds_a[w % NA];
           const uint8_t* prow = sa + i16 * AROW + h * 16 * AROW;
           const uint8_t* psc = sa + A_SC + i16 * 4 + g + h * 64;
-          using ATileT = std::conditional_t<MX, i32x8, u32x4[4]>;
-          auto load_tile = [&](int j, ATileT& aop, int& asc) {  // the wave's j-th tile: row tile h + NPH j
+          auto load_tile = [&](int j, i32x8& aop, int& asc) {  // MXFP8: the wave's j-th tile, row tile h + NPH j
             const uint8_t* pr = prow + j * NPH * 16 * AROW;
-            if constexpr (MX) {
-              const u32x4 lo = *(const u32x4*)(pr + 16 * (g ^ (i16 & SWZ)));
-              const u32x4 hi = *(const u32x4*)(pr + 16 * ((4 + g) ^ (i16 & SWZ)));
-              asc = psc[j * NPH * 64];
-              aop = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-            } else {
-              #pragma unroll
-              for (int st = 0; st < 4; ++st) aop[st] = *(const u32x4*)(pr + 16 * ((4 * g + st) ^ (i16 & SWZ)));
-              asc = 0;
-            }
+            const u32x4 lo = *(const u32x4*)(pr + 16 * (g ^ (i16 & SWZ)));
+            const u32x4 hi = *(const u32x4*)(pr + 16 * ((4 + g) ^ (i16 & SWZ)));
+            asc = psc[j * NPH * 64];
+            aop = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
           };
-          // bf16: the weights as bf16 MFMA operands, converted once per window
-          [[maybe_unused]] bf16x8 bcv[MX ? 1 : PPW][MX ? 1 : 4][MX ? 1 : 4];
-          if constexpr (!MX) {
+          // the step's DMAs are spread over the MFMA groups (the wave keeps the matrix core busy while
+          // the memory pipeline drains); the next group's operands are read before each group of
+          // DMAs, which are compiler barriers for memory operations
+          if constexpr (N == 0) {
+            issue_range.template operator()<0, LPW>(w);
+          } else if constexpr (!MX) {
+            // bf16, one MFMA step (a quarter of the window's K) at a time: the weights of step st + 1
+            // are converted to bf16 and its A operands read ahead of the MFMAs of step st, so after the
+            // window's barrier the matrix core waits for one step's conversion rather than the
+            // whole window's
+            float scl[PPW][4];
             #pragma unroll
             for (int pp = 0; pp < PPW; ++pp)
               #pragma unroll
-              for (int ct = 0; ct < 4; ++ct)
+              for (int ct = 0; ct < 4; ++ct) scl[pp][ct] = e8m0_f32((bsc[pp] >> (8 * ct)) & 0xFFu);
+            u32x4 ac[N], an[N];
+            bf16x8 bc[PPW][4], bn[PPW][4];
+            auto read_slice = [&](const int st, u32x4 (&a)[N], bf16x8 (&b)[PPW][4]) __attribute__((always_inline)) {
+              #pragma unroll
+              for (int j = 0; j < N; ++j)
+                a[j] = *(const u32x4*)(prow + j * NPH * 16 * AROW + 16 * ((4 * g + st) ^ (i16 & SWZ)));
+              #pragma unroll
+              for (int pp = 0; pp < PPW; ++pp)
                 #pragma unroll
-                for (int st = 0; st < 4; ++st)
-                  bcv[pp][ct][st] = fp4_operand(bw[pp][ct][st], e8m0_f32((bsc[pp] >> (8 * ct)) & 0xFFu));
-          }
-          // the step's DMAs are spread over the tiles (the wave keeps the matrix core busy while the
-          // memory pipeline drains); the next tile's operands are read before each group of DMAs,
-          // which are compiler barriers for memory operations
-          if constexpr (N == 0) {
-            issue_range.template operator()<0, LPW>(w);
+                for (int ct = 0; ct < 4; ++ct) b[pp][ct] = fp4_operand(bw[pp][ct][st], scl[pp][ct]);
+            };  // step st: the A operands of the wave's tiles and the weights of its panels
+            read_slice(0, ac, bc);
+            [&]<int... SI>(std::integer_sequence<int, SI...>) {
+              ([&] {
+                constexpr int st = SI;
+                if constexpr (st + 1 < 4) read_slice(st + 1, an, bn);
+                #pragma unroll
+                for (int j = 0; j < N; ++j)
+                  #pragma unroll
+                  for (int pp = 0; pp < PPW; ++pp)
+                    #pragma unroll
+                    for (int ct = 0; ct < 4; ++ct)
+                      acc[j][pp][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ac[j]), bc[pp][ct],
+                                                                                acc[j][pp][ct], 0, 0, 0);
+                issue_range.template operator()<st * LPW / 4, (st + 1) * LPW / 4>(w);
+                if constexpr (st + 1 < 4) {
+                  #pragma unroll
+                  for (int j = 0; j < N; ++j) ac[j] = an[j];
+                  #pragma unroll
+                  for (int pp = 0; pp < PPW; ++pp)
+                    #pragma unroll
+                    for (int ct = 0; ct < 4; ++ct) bc[pp][ct] = bn[pp][ct];
+                }
+              }(), ...);
+            }(std::make_integer_sequence<int, 4>{});
           } else {
-            ATileT cur;
+            // MXFP8: one scaled MFMA per tile and column tile covers the window; the next tile's
+            // operands are read ahead
+            i32x8 cur;
             int csc;
             load_tile(0, cur, csc);
             [&]<int... JI>(std::integer_sequence<int, JI...>) {
               ([&] {
                 constexpr int j = JI;
-                ATileT nxt;
+                i32x8 nxt;
                 int nsc = 0;
                 if constexpr (j + 1 < N) load_tile(j + 1, nxt, nsc);
-                if constexpr (MX) {
+                #pragma unroll
+                for (int pp = 0; pp < PPW; ++pp)
                   #pragma unroll
-                  for (int pp = 0; pp < PPW; ++pp)
-                    #pragma unroll
-                    for (int ct = 0; ct < 4; ++ct) {
-                      const i32x8 bop = {(int)bw[pp][ct][0], (int)bw[pp][ct][1], (int)bw[pp][ct][2], (int)bw[pp][ct][3],
-                                         0, 0, 0, 0};
-                      acc[j][pp][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                          cur, bop, acc[j][pp][ct], 0, 4, 0, csc, 0, (int)(bsc[pp] >> (8 * ct)));
-                    }
-                } else {
-                  #pragma unroll
-                  for (int st = 0; st < 4; ++st) {
-                    const bf16x8 av = __builtin_bit_cast(bf16x8, cur[st]);
-                    #pragma unroll
-                    for (int pp = 0; pp < PPW; ++pp)
-                      #pragma unroll
-                      for (int ct = 0; ct < 4; ++ct)
-                        acc[j][pp][ct] =
-                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bcv[pp][ct][st], acc[j][pp][ct], 0, 0, 0);
+                  for (int ct = 0; ct < 4; ++ct) {
+                    const i32x8 bop = {(int)bw[pp][ct][0], (int)bw[pp][ct][1], (int)bw[pp][ct][2], (int)bw[pp][ct][3],
+                                       0, 0, 0, 0};
+                    acc[j][pp][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        cur, bop, acc[j][pp][ct], 0, 4, 0, csc, 0, (int)(bsc[pp] >> (8 * ct)));
                   }
-                }
                 issue_range.template operator()<j * LPW / N, (j + 1) * LPW / N>(w);
                 if constexpr (j + 1 < N) {
-                  if constexpr (MX) {
-                    cur = nxt;
-                  } else {
-                    #pragma unroll
-                    for (int st = 0; st < 4; ++st) cur[st] = nxt[st];
-                  }
+                  cur = nxt;
                   csc = nsc;
                 }
               }(), ...);
