@@ -957,8 +957,9 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
       // A DMAs of this wave: code instruction j = wv APW + jj covers chunk rows RPD j .. RPD j + RPD - 1
       // (lane L: row RPD j + L / CPR, position L % CPR holding 16-byte chunk (L % CPR) ^ (row & SWZ) of
       // the row's window); MXFP8: the scale instruction covers rows 64 wv .. 64 wv + 63 (lane L: row
-      // 64 wv + L; waves past the chunk's rows send theirs to the sink). Rows past the chunk and
-      // elements past K read zeros.
+      // 64 wv + L; waves past the chunk's rows send theirs to the sink). Elements past K read zeros;
+      // rows past the chunk read zeros, or stale data where a whole piece lies past it (the rows of an
+      // MFMA tile are independent, and those rows' outputs are never stored).
       #pragma unroll
       for (int jj = 0; jj < APW; ++jj) {
         const int row = mb + RPD * (wv * APW + jj) + lane / CPR;
@@ -991,9 +992,16 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
           const u32 st = (u32)((wa % NA) * A_STAGE);
           if (!real)
             dma4<false>(ar, lds_s, kOOB);  // prologue placeholder (4 bytes a lane: the sink holds 256)
-          else if constexpr (d < APW)
-            dma16<false>(ar, a_w + st + 1024 * d,
-                         in && acode[d] >= 0 && kWinK * wa + akel[d] < args.K ? acode[d] + AROW * wa : kOOB);
+          else if constexpr (d < APW) {
+            // grouped: a piece wholly past the chunk's rows becomes a 4-byte dummy into the sink (the
+            // count of DMAs per step stays fixed; its stage rows keep older data, which only rows past
+            // the chunk read). Dense chunks are full but for the last, and the test costs them more.
+            if (!DENSE && mb + RPD * (wv * APW + d) >= r1)  // uniform
+              dma4<false>(ar, lds_s, kOOB);
+            else
+              dma16<false>(ar, a_w + st + 1024 * d,
+                           in && acode[d] >= 0 && kWinK * wa + akel[d] < args.K ? acode[d] + AROW * wa : kOOB);
+          }
           else
             dma4<false>(asr, 64 * wv < ROWS ? a_s + st : lds_s, in && ascale >= 0 ? ascale + 4 * wa : kOOB);
         } else {
@@ -1923,13 +1931,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) acc[t][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // pieces past K (a K tail inside the last window) read zeros
+    // pieces past K (a K tail inside the last window) read zeros; a wave whose share of a tile lies past
+    // the expert's rows (its first row there, uniform) issues no load for it and stages zeros: the load
+    // path is what bounds this kernel, and loads past a buffer's range still cost their issue
+    const int share0 = AFMT == A_BF16 ? 4 * wave : (wave < 2 ? 8 * wave : (wave == 2 ? 0 : 16));
     auto load_rb = [&](RB& b, int wi) {
       load_w(b.w, wr, lane, wi);
       const bool in = wi < nwin;
       const int k0 = kWinK * wi;
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
+        if (share0 >= 16 || mb + 16 * t + share0 >= r1) {  // uniform
+          b.p[t] = u32x4{0u, 0u, 0u, 0u};
+          continue;
+        }
         if constexpr (AFMT == A_BF16) {
           const int off = in && pv[t] && k0 + 8 * pc < args.K ? (parow[t] * (int)args.lda + k0 + 8 * pc) * 2 : kOOB;
           b.p[t] = __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0);
