@@ -11,8 +11,9 @@ RUN_DIR holds
   write/write_counter_collection.csv  --calib-copy-mb 1024), and --pmc WRITE_SIZE likewise
   c*/c*_counter_collection.csv      optional further --pmc passes (SQ_, TA_, TD_, TCP_, TCC_ counters)
 
-Dispatches are grouped by kernel symbol and grid size, so one bench run that times several workloads
-(decode first, then the workload profiled) yields separate rows for the same kernel at each size.
+Dispatches are grouped by kernel symbol, grid size and bench phase (a new phase starts where weights
+are packed after a layer stage has run: each workload a bench run times after the decode batch packs
+its own), so the same kernel at the same grid in two workloads yields two rows.
 """
 from __future__ import annotations
 
@@ -32,8 +33,8 @@ N_XCD, N_CU = 8, 256
 
 
 def stage_of(name: str):
-    if any(k in name for k in ("panel_gemm_kernel", "tiled_gemm_kernel", "tiled_f8_kernel", "skinny_gemm_kernel",
-                               "skinny_reduce_kernel")):
+    if any(k in name for k in ("panel_gemm_kernel", "panel_rows_kernel", "tiled_gemm_kernel", "tiled_f8_kernel",
+                               "skinny_gemm_kernel", "skinny_reduce_kernel")):
         tag = int(name.split(">(")[0].replace("<", ",").split(",")[-1])
         return STAGE[tag] + (" (reduce)" if "skinny_reduce" in name else "")
     if "tile_items" in name:
@@ -47,27 +48,49 @@ def stage_of(name: str):
     return None
 
 
+def phases(rows, name_of, order_of):
+    """Phase of each row in dispatch order: 0 up to the first weight packing that follows a layer stage's
+    kernel, then one more at each such packing (a workload's weights are packed before its steps)."""
+    ph, staged, out = 0, False, []
+    for r in sorted(rows, key=order_of):
+        name = name_of(r)
+        if "pack_kernel" in name and staged:
+            ph += 1
+            staged = False
+        elif stage_of(name) not in (None, "pack"):
+            staged = True
+        out.append((r, ph))
+    return out
+
+
 def trace(path):
-    """(symbol, grid) -> list of durations (ns) from a kernel-trace CSV."""
+    """(symbol, grid, phase) -> list of durations (ns) from a kernel-trace CSV."""
     per = collections.defaultdict(list)
-    for r in csv.DictReader(open(path)):
+    rows = list(csv.DictReader(open(path)))
+    for r, ph in phases(rows, lambda r: r["Kernel_Name"], lambda r: int(r["Start_Timestamp"])):
         g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
-        per[(r["Kernel_Name"], g)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        per[(r["Kernel_Name"], g, ph)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     return per
 
 
 def counter_passes(path):
-    """(symbol, grid) -> {counter: mean value per dispatch}, and the calibration copy's values."""
+    """(symbol, grid, phase) -> {counter: mean value per dispatch}, and the calibration copy's values."""
     acc = collections.defaultdict(lambda: collections.defaultdict(float))
     disp = collections.defaultdict(lambda: collections.defaultdict(set))
     calib = {}
-    for r in csv.DictReader(open(path)):
+    rows = list(csv.DictReader(open(path)))
+    # phases over dispatches (a dispatch has one row per counter)
+    first = {}
+    for r in rows:
+        first.setdefault(int(r["Dispatch_Id"]), r["Kernel_Name"])
+    ph_of = {d: ph for (d, _), ph in phases(list(first.items()), lambda dn: dn[1], lambda dn: dn[0])}
+    for r in rows:
         name, c, v = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
         if "copyBuffer" in name:
             # the calibration copy (the bench's only large device copy)
             calib[c] = max(calib.get(c, 0.0), v)
             continue
-        key = (name, int(r["Grid_Size"]))
+        key = (name, int(r["Grid_Size"]), ph_of[int(r["Dispatch_Id"])])
         acc[key][c] += v
         disp[key][c].add(r["Dispatch_Id"])
     return {k: {c: v / len(disp[k][c]) for c, v in d.items()} for k, d in acc.items()}, calib
@@ -114,31 +137,34 @@ def main():
              "```", cmd, "```", "",
              f"Calibration: the 1 GiB device copy in the same run reads FETCH_SIZE = {cf['FETCH_SIZE']:.0f} KiB and "
              f"WRITE_SIZE = {cw['WRITE_SIZE']:.0f} KiB, so FETCH_SIZE is scaled by {ff:.4f} and WRITE_SIZE by {fw:.4f}.",
-             "", "Dispatches are grouped by kernel and grid size (blocks x threads).", "",
-             "| kernel | grid | stage | calls | avg us | FETCH KiB/dispatch | WRITE KiB/dispatch | HBM bytes/dispatch (calibrated) |",
-             "|---|---|---|---|---|---|---|---|"]
+             "", "Dispatches are grouped by kernel, grid size (blocks x threads) and bench phase (the "
+             "decode batch is phase 1, after the plain streaming read of phase 0; each later workload packs its "
+             "weights first and starts the next phase).", "",
+             "| kernel | grid | phase | stage | calls | avg us | FETCH KiB/dispatch | WRITE KiB/dispatch | HBM bytes/dispatch (calibrated) |",
+             "|---|---|---|---|---|---|---|---|---|"]
     rec = {"kernels_hip_sha256": hashlib.sha256(open(os.path.join(HERE, "csrc", "kernels.hip"), "rb").read()).hexdigest(),
            "fetch_scale": ff, "write_scale": fw, "kernels": {}}
     rows = sorted(kern.items(), key=lambda kv: -sum(kv[1]))
     # the stage's kernel of this workload: its (symbol, grid) of the longest mean duration (a bench run
     # that profiles prefill also times the decode batch first, whose launches are far shorter)
     best = {}
-    for (n, g), d in rows:
-        st = stage_of(n)
+    for key, d in rows:
+        st = stage_of(key[0])
         if st in STAGE.values() and (st not in best or sum(d) / len(d) > best[st][1]):
-            best[st] = ((n, g), sum(d) / len(d))
-    for (n, g), d in rows:
+            best[st] = (key, sum(d) / len(d))
+    for key, d in rows:
+        n, g, ph = key
         st = stage_of(n)
         avg = sum(d) / len(d)
-        fk = fetch.get((n, g), {}).get("FETCH_SIZE")
-        wk = write.get((n, g), {}).get("WRITE_SIZE")
+        fk = fetch.get(key, {}).get("FETCH_SIZE")
+        wk = write.get(key, {}).get("WRITE_SIZE")
         tb = (fk * ff + wk * fw) * 1024 if fk is not None and wk is not None else None
-        lines.append(f"| `{n[:78]}` | {g} | {st or ''} | {len(d)} | {avg / 1000:.1f} | "
+        lines.append(f"| `{n[:78]}` | {g} | {ph} | {st or ''} | {len(d)} | {avg / 1000:.1f} | "
                      f"{'' if fk is None else f'{fk:.0f}'} | {'' if wk is None else f'{wk:.0f}'} | "
                      f"{'' if tb is None else f'{tb:.4g}'} |")
-        if st in best and best[st][0] == (n, g) and tb is not None:
-            rec["kernels"][st] = {"symbol": n, "grid": g, "avg_us": avg / 1000, "fetch_kib": fk, "write_kib": wk,
-                                  "hbm_bytes_per_launch": tb}
+        if st in best and best[st][0] == key and tb is not None:
+            rec["kernels"][st] = {"symbol": n, "grid": g, "phase": ph, "avg_us": avg / 1000, "fetch_kib": fk,
+                                  "write_kib": wk, "hbm_bytes_per_launch": tb}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     open(os.path.join(ROOT, "profiles", f"kernels_{workload}.md"), "w").write("\n".join(lines) + "\n")
     json.dump(rec, open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"), "w"), indent=1)
@@ -160,7 +186,7 @@ def main():
           "the kernel's duration gives the clock); SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs; TA/TD/TCP "
           "busy and stall counts over the 256 CUs.", ""]
     for st, r in rec["kernels"].items():
-        key = (r["symbol"], r["grid"])
+        key = (r["symbol"], r["grid"], r["phase"])
         c = merged.get(key)
         if not c:
             continue
