@@ -1290,9 +1290,12 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
 // Block: 8 waves (2 per SIMD) on one expert's chunk of up to 192 rows and 4 consecutive panels; wave
 // (pg, h) computes panel panel0 + pg on row tiles h, h + 2, ... (6 row tiles x 4 column tiles of 16).
 // Per 128-K window:
-//   - the wave's own panel-window is loaded straight into a register ring DB windows ahead with the
-//     non-temporal policy (the weights stream from HBM once): each lane's 16 bytes are already its MFMA
-//     operand, so the weights never pass through LDS;
+//   - the two waves of a panel split its panel-window: wave h loads weight row-tiles 2h and 2h + 1 (and
+//     the scale word) straight into a register ring DB windows ahead with the non-temporal policy (the
+//     weights stream from HBM once; each lane's 16 bytes are already its MFMA operand), writes its two
+//     row-tiles to an LDS stage at the end of the window before they are used and reads the partner's two from
+//     there; so each weight byte passes the CU's load path once (the load path, about 64 bytes a
+//     clock per CU, is the kernel's tightest unit; LDS reads run at about three times that rate);
 //   - the chunk's activation rows (E4M3 codes and E8M0 scales, mostly L2 hits: the expert's other
 //     panel blocks read the same rows) are loaded into registers DA windows ahead, each wave 24 rows
 //     (three 16-byte pieces a lane; waves 0..2 also one scale word a lane), and written to one of two
@@ -1311,6 +1314,7 @@ void tiled_f8_kernel(GemmArgs args) {
   constexpr int ROWS = 16 * MT, NPG = 4, NPH = NWAVE / NPG, MTW = MT / NPH;
   constexpr int AROW = 128, A_SC = ROWS * AROW, A_STAGE = A_SC + ROWS * 4;
   constexpr int NB = DB + 1;
+  static_assert(NPH == 2, "the two waves of a panel share its weight windows");
   constexpr int APL = ROWS * AROW / (16 * 64 * NWAVE);  // 16-byte activation pieces per lane and window
   constexpr int SCW = ROWS / 64;                         // waves that load a scale word per lane
   constexpr int U = NB % 2 == 0 ? NB : 2 * NB;           // windows per unrolled step (stage, set, slot cycle)
@@ -1319,10 +1323,14 @@ void tiled_f8_kernel(GemmArgs args) {
   static_assert(ROWS * 132 <= A_STAGE, "epilogue staging fits one stage");
   static_assert(EPI == 0 || EPI == 1, "epilogue");
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][A_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][NPG][4096];  // weight codes, row-tile rt at 1024 rt
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int pg = wv % NPG, h = wv / NPG;
+  // column tile (weight row-tile) of the wave's MFMA slot q: its own two row-tiles first, then the
+  // partner's (uniform over the wave)
+  auto ctq = [&](int q) __attribute__((always_inline)) { return q < 2 ? 2 * h + q : 2 * (1 - h) + q - 2; };
   const int g = lane >> 4, i16 = lane & 15;
   const rsrc_t ar = make_rsrc(args.A, args.a_bytes);
   const rsrc_t asr = make_rsrc(args.A_scales, args.as_bytes);
@@ -1394,12 +1402,12 @@ void tiled_f8_kernel(GemmArgs args) {
     u32x4 c[APL];
     u32 sc;
   };
-  struct BWinR {  // one window of this wave's panel
-    u32x4 c[4];
+  struct BHalfR {  // one window of this wave's half of its panel: row-tiles 2h, 2h + 1 and the scales
+    u32x4 c[2];
     u32 sc;
   };
   AWinR ast[DA];
-  BWinR bring[NB];
+  BHalfR bring[NB];
   // The window index passes through an empty asm statement: the offsets are then formed where the loads
   // are issued instead of being precomputed for every unrolled window (which would hold them in VGPRs).
   auto load_a = [&](AWinR& a, int w) __attribute__((always_inline)) {
@@ -1416,12 +1424,17 @@ void tiled_f8_kernel(GemmArgs args) {
     for (int j = 0; j < APL; ++j) *(u32x4*)(base + 1024 * (APL * wv + j) + 16 * lane) = a.c[j];
     if (wv < SCW) *(u32*)(base + A_SC + 256 * wv + 4 * lane) = a.sc;
   };
-  auto load_b = [&](BWinR& b, int w) __attribute__((always_inline)) {
+  auto load_b = [&](BHalfR& b, int w) __attribute__((always_inline)) {
     asm volatile("" : "+s"(w));
     const int off = w < nwin ? w * kPanelWinBytes : kOOB;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) b.c[rt] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + rt * 1024 + lane * 16, 0, kNT);
+    for (int i = 0; i < 2; ++i)
+      b.c[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, off + (2 * h + i) * 1024 + lane * 16, 0, kNT);
     b.sc = __builtin_amdgcn_raw_buffer_load_b32(wr, off + 4096 + lane * 4, 0, kNT);
+  };
+  auto store_b = [&](const BHalfR& b, int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *(u32x4*)(&lds_b[stage][pg][(2 * h + i) * 1024 + 16 * lane]) = b.c[i];
   };
   // first loads of a unit: A(0), A(1) into the staging sets, B(0 .. DB - 1) into the ring
   auto prologue_loads = [&]() __attribute__((always_inline)) {
@@ -1430,9 +1443,11 @@ void tiled_f8_kernel(GemmArgs args) {
 #pragma unroll
     for (int n = 0; n < DB; ++n) load_b(bring[n], n);
   };
-  // A(0) to stage 0, then A(DA) into the set it came from (one set: A(1) once A(0) is written)
+  // A(0) and this wave's half of B(0) to stage 0, then A(DA) into the set it came from (one set: A(1)
+  // once A(0) is written)
   auto prologue_store = [&]() __attribute__((always_inline)) {
     store_a(ast[0], 0);
+    store_b(bring[0], 0);
     load_a(ast[0], DA);
   };
 
@@ -1457,12 +1472,18 @@ void tiled_f8_kernel(GemmArgs args) {
             constexpr int u = UI;
             const int w = w0 + u;
             if (w < nwin) {  // uniform
-              lds_barrier();  // A(w) in its stage for every wave; every wave done with window w - 1
+              lds_barrier();  // A(w), B(w) in their stages for every wave; every wave done with window w - 1
               if (w + 1 < nwin) store_a(ast[(u + 1) % DA], (u + 1) & 1);
               load_a(ast[(u + 1) % DA], w + 1 + DA);
               load_b(bring[(u + DB) % NB], w + DB);
               if constexpr (N > 0) {
-                const BWinR& bw = bring[u % NB];
+                const BHalfR& bw = bring[u % NB];
+                // the partner's two row-tiles of B(w)
+                const uint8_t* sbp = &lds_b[u & 1][pg][(2 - 2 * h) * 1024 + 16 * lane];
+                const u32x4 bo[2] = {*(const u32x4*)sbp, *(const u32x4*)(sbp + 1024)};
+                int bsq[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) bsq[q] = (int)(bw.sc >> (8 * ctq(q)));
                 const uint8_t* sa = lds_a[u & 1];
                 const uint8_t* prow = sa + i16 * AROW + h * 16 * AROW;
                 const uint8_t* psc = sa + A_SC + i16 * 4 + g + h * 64;
@@ -1483,10 +1504,11 @@ void tiled_f8_kernel(GemmArgs args) {
                     int nsc = 0;
                     if constexpr (j + 1 < N) tile(j + 1, nxt, nsc);
 #pragma unroll
-                    for (int ct = 0; ct < 4; ++ct) {
-                      const i32x8 bop = {(int)bw.c[ct][0], (int)bw.c[ct][1], (int)bw.c[ct][2], (int)bw.c[ct][3], 0, 0, 0, 0};
-                      acc[j][ct] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur, bop, acc[j][ct], 0, 4, 0, csc, 0,
-                                                                                    (int)(bw.sc >> (8 * ct)));
+                    for (int q = 0; q < 4; ++q) {
+                      const u32x4 bq = q < 2 ? bw.c[q] : bo[q - 2];
+                      const i32x8 bop = {(int)bq[0], (int)bq[1], (int)bq[2], (int)bq[3], 0, 0, 0, 0};
+                      acc[j][q] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur, bop, acc[j][q], 0, 4, 0, csc, 0,
+                                                                                   bsq[q]);
                     }
                     if constexpr (j + 1 < N) {
                       cur = nxt;
@@ -1495,6 +1517,9 @@ void tiled_f8_kernel(GemmArgs args) {
                   }(), ...);
                 }(std::make_integer_sequence<int, N>{});
               }
+              // this wave's half of B(w + 1) to its stage after the window's MFMAs: its loads, issued two
+              // windows before it is used, have had the most time to land
+              if (w + 1 < nwin) store_b(bring[(u + 1) % NB], (u + 1) & 1);
             }
           }(), ...);
         }(std::make_integer_sequence<int, U>{});
@@ -1525,10 +1550,11 @@ void tiled_f8_kernel(GemmArgs args) {
           const int row0 = e_mb + 16 * (h + NPH * j) + 4 * eg;
           if (pg < e_npan && row0 < e_r1) {
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
+            for (int q = 0; q < 4; ++q) {
+              const int ct = ctq(q);
               const int col = EPI == 1 ? 32 * (e_panel0 + pg) + 16 * (ct >> 1) + ej : 64 * (e_panel0 + pg) + 16 * ct + ej;
               const int q0 = EPI == 1 && (ct & 1) ? args.lora_rank : 0;
-              lora_add(args, acc[j][ct], e_grp, row0, e_r1, col, q0);
+              lora_add(args, acc[j][q], e_grp, row0, e_r1, col, q0);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -1544,8 +1570,10 @@ void tiled_f8_kernel(GemmArgs args) {
         for (int j = 0; j < MTW; ++j) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float v0 = silu(acc[j][0][r]) * acc[j][1][r];
-            const float v1 = silu(acc[j][2][r]) * acc[j][3][r];
+            // slots 0, 1 hold gate and up of units 32 p + 16 h + ej, slots 2, 3 those of the other half
+            const float va = silu(acc[j][0][r]) * acc[j][1][r];
+            const float vb = silu(acc[j][2][r]) * acc[j][3][r];
+            const float v0 = h ? vb : va, v1 = h ? va : vb;  // units 32 p + ej and 32 p + 16 + ej
             const int lr = 16 * (h + NPH * j) + 4 * eg + r;
             if (tap) {
               const int o = lr * (int)sg.ldpre + sg.col0 + 32 * (e_panel0 + pg) + ej;
@@ -1589,9 +1617,10 @@ void tiled_f8_kernel(GemmArgs args) {
             const int base = 4 * (lr * ldo + 64 * (e_panel0 + pg) + ej);
             const bool rok = lr < nrow && pg < e_npan;
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
+            for (int q = 0; q < 4; ++q) {
+              const int ct = ctq(q);
               const bool ok = rok && 64 * (e_panel0 + pg) + 16 * ct + ej < sg.ncols;
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][ct][r]), orr, ok ? base + 64 * ct : kOOB, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][q][r]), orr, ok ? base + 64 * ct : kOOB, 0, 0);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -2155,7 +2184,8 @@ static void launch_f8(const GemmArgs& a, hipStream_t s) {
     // down (fp32 out): both operands through LDS-DMA; activation rows 3 windows ahead, weights 2
     launch_grouped_tiled<3, 2, 12, EPI, TAG, A_MXFP8>(a, s);
   } else {
-    // gate/up: 192-row chunks on 8 waves, weights 2 windows ahead in registers, activation rows 2 ahead
+    // gate/up: 192-row chunks on 8 waves, half panel-windows 2 windows ahead in registers, activation
+    // rows 2 ahead
     constexpr int NW = 8, MT = 12, DB = 2, DA = 2;
     const unsigned nblk = (unsigned)ceil_div(a.P, 4);
     unsigned grid = (unsigned)ceil_div(a.n_groups, 8) * 8 * nblk;
