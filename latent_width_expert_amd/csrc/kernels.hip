@@ -1324,6 +1324,7 @@ void tiled_f8_kernel(GemmArgs args) {
   static_assert(EPI == 0 || EPI == 1, "epilogue");
   __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][A_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][NPG][4096];  // weight codes, row-tile rt at 1024 rt
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sink[256];          // scale words of waves without scales
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1416,13 +1417,15 @@ void tiled_f8_kernel(GemmArgs args) {
 #pragma unroll
     for (int j = 0; j < APL; ++j)
       a.c[j] = __builtin_amdgcn_raw_buffer_load_b128(ar, in && aoff[j] >= 0 ? aoff[j] + AROW * w : kOOB, 0, 0);
-    if (wv < SCW) a.sc = __builtin_amdgcn_raw_buffer_load_b32(asr, in && soff >= 0 ? soff + 4 * w : kOOB, 0, 0);
+    // every wave issues the scale load (zeros past the chunk's scale rows), so the count of loads per
+    // window is the same on every path and the compiler's load waits stay exact
+    a.sc = __builtin_amdgcn_raw_buffer_load_b32(asr, in && soff >= 0 ? soff + 4 * w : kOOB, 0, 0);
   };
   auto store_a = [&](const AWinR& a, int stage) __attribute__((always_inline)) {
     uint8_t* base = &lds_a[stage][0];
 #pragma unroll
     for (int j = 0; j < APL; ++j) *(u32x4*)(base + 1024 * (APL * wv + j) + 16 * lane) = a.c[j];
-    if (wv < SCW) *(u32*)(base + A_SC + 256 * wv + 4 * lane) = a.sc;
+    *(u32*)((wv < SCW ? base + A_SC + 256 * wv : &lds_sink[0]) + 4 * lane) = a.sc;
   };
   auto load_b = [&](BHalfR& b, int w) __attribute__((always_inline)) {
     asm volatile("" : "+s"(w));
@@ -1465,6 +1468,9 @@ void tiled_f8_kernel(GemmArgs args) {
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) acc[j][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // The window loop, U windows unrolled. No load or stage write sits under a branch inside a window (at
+    // the last window the stage writes carry the zeros of windows past K into stages nobody reads), so
+    // the compiler's load waits cover exactly what each use needs rather than the loads just issued.
     auto run = [&]<int N>() __attribute__((always_inline)) {
       for (int w0 = 0; w0 < nwin; w0 += U) {
         [&]<int... UI>(std::integer_sequence<int, UI...>) __attribute__((always_inline)) {
@@ -1473,7 +1479,7 @@ void tiled_f8_kernel(GemmArgs args) {
             const int w = w0 + u;
             if (w < nwin) {  // uniform
               lds_barrier();  // A(w), B(w) in their stages for every wave; every wave done with window w - 1
-              if (w + 1 < nwin) store_a(ast[(u + 1) % DA], (u + 1) & 1);
+              store_a(ast[(u + 1) % DA], (u + 1) & 1);
               load_a(ast[(u + 1) % DA], w + 1 + DA);
               load_b(bring[(u + DB) % NB], w + DB);
               if constexpr (N > 0) {
@@ -1519,7 +1525,7 @@ void tiled_f8_kernel(GemmArgs args) {
               }
               // this wave's half of B(w + 1) to its stage after the window's MFMAs: its loads, issued two
               // windows before it is used, have had the most time to land
-              if (w + 1 < nwin) store_b(bring[(u + 1) % NB], (u + 1) & 1);
+              store_b(bring[(u + 1) % NB], (u + 1) & 1);
             }
           }(), ...);
         }(std::make_integer_sequence<int, U>{});
