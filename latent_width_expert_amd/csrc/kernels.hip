@@ -1570,31 +1570,39 @@ void tiled_f8_kernel(GemmArgs args) {
         // codes staged as [ROWS][128 bytes] (32 units per panel), scales as [ROWS][4]
         uint8_t* stg = &lds_a[0][0];
         uint8_t* stg_sc = stg + ROWS * 128;
-        const bool tap = sg.pre != nullptr;
-        const rsrc_t prr = make_rsrc(tap ? sg.pre + (int64_t)e_mb * sg.ldpre : nullptr, tap ? (int64_t)nrow * sg.ldpre * 4 : 0);
+        // slots 0, 1 hold gate and up of units 32 pg + 16 h + ej (staging column ca), slots 2, 3 those of
+        // units 32 pg + 16 (1 - h) + ej (column cb); the MX block is the 32 units of the panel either way
+        const int ca = 32 * pg + 16 * h + ej, cb = 32 * pg + 16 * (1 - h) + ej;
+        // TAP: also the fp32 SwiGLU values (a test tap); a separate copy of the loop, so the untapped one
+        // carries none of its stores or branches
+        auto glu = [&]<bool TAP>() __attribute__((always_inline)) {
+          const rsrc_t prr = make_rsrc(TAP ? sg.pre + (int64_t)e_mb * sg.ldpre : nullptr, TAP ? (int64_t)nrow * sg.ldpre * 4 : 0);
 #pragma unroll
-        for (int j = 0; j < MTW; ++j) {
+          for (int j = 0; j < MTW; ++j) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            // slots 0, 1 hold gate and up of units 32 p + 16 h + ej, slots 2, 3 those of the other half
-            const float va = silu(acc[j][0][r]) * acc[j][1][r];
-            const float vb = silu(acc[j][2][r]) * acc[j][3][r];
-            const float v0 = h ? vb : va, v1 = h ? va : vb;  // units 32 p + ej and 32 p + 16 + ej
-            const int lr = 16 * (h + NPH * j) + 4 * eg + r;
-            if (tap) {
-              const int o = lr * (int)sg.ldpre + sg.col0 + 32 * (e_panel0 + pg) + ej;
-              const bool ok = lr < nrow && pg < e_npan;
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), prr, ok ? 4 * o : kOOB, 0, 0);
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), prr, ok ? 4 * (o + 16) : kOOB, 0, 0);
+            for (int r = 0; r < 4; ++r) {
+              const float va = silu(acc[j][0][r]) * acc[j][1][r];
+              const float vb = silu(acc[j][2][r]) * acc[j][3][r];
+              const int lr = 16 * (h + NPH * j) + 4 * eg + r;
+              if constexpr (TAP) {
+                const int o = lr * (int)sg.ldpre + sg.col0 + 32 * e_panel0;
+                const bool ok = lr < nrow && pg < e_npan;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(va), prr, ok ? 4 * (o + ca) : kOOB, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vb), prr, ok ? 4 * (o + cb) : kOOB, 0, 0);
+              }
+              u32 c0, c1, sb;
+              mxfp8_block(va, vb, c0, c1, sb);
+              stg[lr * 128 + ca] = (uint8_t)c0;
+              stg[lr * 128 + cb] = (uint8_t)c1;
+              if (ej == 0) stg_sc[lr * 4 + pg] = (uint8_t)sb;  // the 16 lanes of the block agree
             }
-            u32 c0, c1, sb;
-            mxfp8_block(v0, v1, c0, c1, sb);
-            stg[lr * 128 + 32 * pg + ej] = (uint8_t)c0;
-            stg[lr * 128 + 32 * pg + 16 + ej] = (uint8_t)c1;
-            if (ej == 0) stg_sc[lr * 4 + pg] = (uint8_t)sb;  // the 16 lanes of the block agree
+            __builtin_amdgcn_sched_barrier(0);
           }
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        };
+        if (sg.pre)
+          glu.template operator()<true>();
+        else
+          glu.template operator()<false>();
         lds_barrier();
         const int t = threadIdx.x;
         uint8_t* out = (uint8_t*)sg.out + sg.col0 + 32 * e_panel0;
