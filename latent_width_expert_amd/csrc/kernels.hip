@@ -1293,16 +1293,17 @@ __global__ __launch_bounds__(256 * WPS) void tiled_gemm_kernel(GemmArgs args) {
 //   - the two waves of a panel split its panel-window: wave h loads weight row-tiles 2h and 2h + 1 (and
 //     the scale word) straight into a register ring DB windows ahead with the non-temporal policy (the
 //     weights stream from HBM once; each lane's 16 bytes are already its MFMA operand), writes its two
-//     row-tiles to an LDS stage at the end of the window before they are used and reads the partner's two from
-//     there; so each weight byte passes the CU's load path once (the load path, about 64 bytes a
-//     clock per CU, is the kernel's tightest unit; LDS reads run at about three times that rate);
+//     row-tiles to an LDS stage at the end of the window before they are used and reads the partner's
+//     two from there; so each weight byte passes the CU's load path once (that path moves about 55-64
+//     bytes a clock per CU, LDS reads about three times as much);
 //   - the chunk's activation rows (E4M3 codes and E8M0 scales, mostly L2 hits: the expert's other
 //     panel blocks read the same rows) are loaded into registers DA windows ahead, each wave 24 rows
-//     (three 16-byte pieces a lane; waves 0..2 also one scale word a lane), and written to one of two
-//     LDS stages the window before they are used (16-byte chunk c of row r at position c ^ (r & 7), so
-//     the operand reads are conflict-free); all eight waves read the operands of their tiles from it.
-// Every load is compiler-visible, so the compiler's waits cover exactly the loads a use depends on;
-// one LDS wait and one barrier per window order the stages. Units (expert, chunk, panel block) come
+//     (three 16-byte pieces a lane, and one scale word a lane: real for waves 0..2, an out-of-range
+//     load for the others), and written to one of two LDS stages the window before they are used
+//     (16-byte chunk c of row r at position c ^ (r & 7), so the operand reads are conflict-free); all
+//     eight waves read the operands of their tiles from it.
+// Every load is compiler-visible and none sits under a branch inside a window, so the compiler's waits
+// cover the loads a use depends on; one LDS wait and one barrier per window order the stages. Units (expert, chunk, panel block) come
 // from the XCD's work-item list as in tiled_gemm_kernel; the next unit's first loads are issued before
 // the current unit's epilogue.
 // EPI 0: fp32 out. EPI 1: GLU panels, SiLU(gate) * up MX-encoded (E4M3, E8M0 per 32 units), staged in
