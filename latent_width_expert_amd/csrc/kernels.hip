@@ -2340,7 +2340,7 @@ hipError_t launch_panel_gemm(const GemmArgs& a, GemmStage stage, hipStream_t s) 
       else if (gu)
         launch_grouped_panel<A_MXFP8, 3, GEMM_GATEUP>(pa, s);
       else if (bf)
-        launch_grouped_panel<A_BF16, 3, GEMM_DOWN>(pa, s);
+        launch_grouped_panel<A_BF16, 4, GEMM_DOWN>(pa, s);  // weights 3 windows ahead
       else
         launch_grouped_panel<A_MXFP8, 3, GEMM_DOWN>(pa, s);
       break;
